@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them.
+
+Each mutation rewrites one snippet of one oracle function's source, compiles
+the result into the oracle module's namespace and patches it in; then every
+pin runs and at least one must fail.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.layer as L
+from oracle_pins import ALL_PINS
+
+MUTATIONS = [
+    # (id, function, snippet as written, planted mistake)
+    ("scale_1_over_d", "attend_union", "1.0 / math.sqrt(q.shape[-1])", "1.0 / q.shape[-1]"),
+    ("no_normaliser", "attend_union", "return num / den,", "return num,"),
+    ("keys_as_values", "attend_union", "num += p @ np.asarray(v,", "num += p @ np.asarray(k,"),
+    ("frame_off_by_one", "frame_attention", "keys = slice(f * L, (f + 1) * L)",
+     "keys = slice(f * L, (f + 1) * L + 1)"),
+    ("window_no_clip_rows", "window_table", "min(block * by + block, gh)", "block * by + block"),
+    ("window_transposed", "window_table", "rows.append(f * L + S + r * gw + c)",
+     "rows.append(f * L + S + c * gh + r)"),
+    ("pool_counts_padding", "compress",
+     "kc[j] = np.asarray(k[rows], dtype=np.float64).mean(axis=0)",
+     "kc[j] = np.asarray(k[rows], dtype=np.float64).sum(axis=0) / block ** 2"),
+    ("no_special_query_block", "query_block_table", "        if S:\n", "        if False:\n"),
+    ("block_score_unscaled", "block_scores", "/ math.sqrt(d)", ""),
+    ("topk_ties_high", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (-row[j], -j)"),
+    ("topk_rank_order", "select_topk", "np.sort(np.array(order[:top_k], dtype=np.int32))",
+     "np.array(order[:top_k], dtype=np.int32)"),
+    ("topk_smallest", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (row[j], j)"),
+    ("fine_drops_specials", "fine_attention", "if use_spec:", "if False:"),
+    ("gate_swapped", "gate", "g[..., 0:1] * np.asarray(o_cmp", "g[..., 1:2] * np.asarray(o_cmp"),
+    ("gate_no_bias", "gate", " + np.asarray(b, np.float64)", ""),
+    ("sga_phase_1", "subsample_plan", "r % s_h == 0 and c % s_w == 0",
+     "r % s_h == 1 % s_h and c % s_w == 0"),
+    ("sga_mean_over_all", "sga_compact", "drop_rows = [base + p for p in dropped]",
+     "drop_rows = [base + p for p in dropped + kept]"),
+    ("sga_own_frame_twice", "subsampled_attention",
+     "s_c[i, f * m:(f + 1) * m] = -np.inf", "pass"),
+    ("sga_mean_token_dropped", "sga_compact", "        if dropped:\n", "        if False:\n"),
+    ("sga_log_count_wrong", "subsampled_attention", "math.log(len(dropped))",
+     "math.log(len(dropped) + 1)"),
+]
+
+
+def _mutant(func_name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(L, func_name)))
+    assert src.count(old) >= 1, f"snippet not found in {func_name}: {old!r}"
+    src = src.replace(old, new)
+    ns = {}
+    exec(compile(src, f"<mutant {func_name}>", "exec"), L.__dict__, ns)
+    return ns[func_name]
+
+
+@pytest.mark.parametrize("mid,func,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, mid, func, old, new):
+    monkeypatch.setattr(L, func, _mutant(func, old, new))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # AssertionError, or the mutant breaking outright
+            caught.append((pin.__name__, type(e).__name__))
+    assert caught, f"no pin caught mutation {mid}"
