@@ -1,0 +1,173 @@
+/*
+ * sga.h -- C ABI of the global cross-frame attention layer on MI355X (gfx950).
+ *
+ * One layer of a VGGT-style multi-view reconstruction transformer in which the
+ * tokens of all N frames attend to each other, in three forms:
+ *   - dense softmax attention (and its per-frame variant),
+ *   - Speed3R global sparse attention (GSA): pooled K/V, compressed attention,
+ *     top-K block selection, fine attention on the selected blocks, a gate,
+ *   - AVGGT subsampled global attention.
+ *
+ * Tensor layout (every Q/K/V/O argument): [rows, n_heads, head_dim], contiguous,
+ * element (t, h, c) at offset (t * n_heads + h) * head_dim + c. Token order:
+ * frame-major; inside a frame the n_special special tokens (camera first, then
+ * registers) precede the grid_h x grid_w patches in row-major order.
+ * Notation: L = n_special + grid_h * grid_w, T = n_frames * L.
+ *
+ * Ownership: every buffer is device memory allocated by the caller; the
+ * library never allocates, frees or retains a caller pointer. Scratch space
+ * comes only through an explicit workspace argument.
+ * Streams: every call enqueues its kernels on `stream` (a hipStream_t; NULL is
+ * the default stream) and returns without synchronising.
+ * Errors: all arguments are validated on the host before anything is
+ * enqueued; on a non-OK status nothing was enqueued and sga_last_error()
+ * describes the problem. A failed launch returns SGA_ERR_HIP. Pointers must
+ * be 16-byte aligned. Only head_dim == 64 is supported.
+ */
+#ifndef SGA_H
+#define SGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SGA_OK = 0,
+  SGA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer     */
+  SGA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement    */
+  SGA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  SGA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
+} sga_status;
+
+typedef enum { SGA_BF16 = 0, SGA_F32 = 1 } sga_dtype;
+
+typedef struct {
+  int32_t n_frames;  /* N >= 1                                             */
+  int32_t n_special; /* S special tokens per frame, 0..16                  */
+  int32_t grid_h;    /* patch grid rows >= 1                               */
+  int32_t grid_w;    /* patch grid columns >= 1                            */
+  int32_t n_heads;   /* H >= 1                                             */
+  int32_t head_dim;  /* d, must be 64                                      */
+  int32_t dtype;     /* sga_dtype of Q/K/V/O and pooled K/V                */
+} sga_geom;
+
+/*
+ * Dense global attention (VGG-T3 technical summary section 1; Speed3R
+ * technical summary section 1; AVGGT technical summary section 1):
+ *   O[t,h] = sum_u softmax_u(Q[t,h] . K[u,h] / sqrt(d)) V[u,h].
+ * q, o:   [T, H, d].   k, v: [n_keys, H, d]; n_keys == 0 means T.
+ * frame_local == 1 restricts the keys of a query to its own frame (the
+ *   global-to-frame conversion of AVGGT section 2.2); requires n_keys == 0.
+ * A nonzero n_keys with other K/V tensors serves the GSA compressed branch
+ *   (Speed3R section 2.1): k, v = the pooled K/V of gsa_compress and
+ *   n_keys = N * nb.
+ * lse (nullable): [T, H] fp32, natural-log log-sum-exp of the scaled logits.
+ */
+sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
+                             const void* v, int64_t n_keys, int32_t frame_local,
+                             void* o, float* lse, void* stream);
+
+/*
+ * GSA compression (Speed3R section 2.1, compression branch): block x block
+ * average pooling of K and V over the patch grid, averaging only the tokens
+ * that fall inside the grid. Only block == 4 is supported.
+ *   nbh = ceil(grid_h/4), nbw = ceil(grid_w/4), nb = nbh*nbw,
+ *   nqb = nb + (n_special > 0 ? 1 : 0).
+ * Pooled key j = f*nb + by*nbw + bx covers patch rows 4by..4by+3 and columns
+ * 4bx..4bx+3 of frame f. Special tokens are not pooled.
+ * k_cmp, v_cmp: [N*nb, H, d] in geom->dtype (rounded once).
+ * k_cmp_f32 (nullable): [N*nb, H, d] fp32 pooled keys (input of selection).
+ * q_blk_f32 (nullable; needs q): [N*nqb, H, d] fp32 mean query of every query
+ *   block: the windows of a frame in pooled-key order, then one block holding
+ *   the frame's special tokens.
+ */
+sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q,
+                        const void* k, const void* v, void* k_cmp, void* v_cmp,
+                        float* k_cmp_f32, float* q_blk_f32, void* stream);
+
+/*
+ * GSA block selection (Speed3R section 2.1, selection branch; the Italian
+ * summary's S_guide score matrix): per head h and query block b the score of
+ * pooled key j is q_blk[b,h] . k_cmp[j,h] / sqrt(d) (the mean over the block's
+ * tokens of their compressed logits); the top_k best j are kept, ties going to
+ * the lower j. The score matrix is never materialised.
+ * idx:   [H, N*nqb, top_k] int32, each row sorted ascending.
+ * score (nullable): [H, N*nqb, top_k] fp32, the score of each idx entry.
+ * 1 <= top_k <= min(N*nb, 128).
+ */
+sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                           const float* k_cmp_f32, int32_t top_k, int32_t* idx,
+                           float* score, void* stream);
+
+/*
+ * GSA fine attention (Speed3R section 2.1, selection branch): each query of
+ * query block b attends to the in-grid tokens of the pooled blocks listed in
+ * idx[h, b, :] and, when keep_special == 1, to every special token of every
+ * frame (the camera tokens kept by the VGGT adaptation in the Italian summary;
+ * special tokens kept in AVGGT section 2.2).
+ * idx: [H, N*nqb, top_k] int32 entries in [0, N*nb), distinct within a row.
+ * o_slc: [T, H, d]. lse (nullable): [T, H] fp32.
+ */
+sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q,
+                           const void* k, const void* v, const int32_t* idx,
+                           int32_t top_k, int32_t keep_special, void* o_slc,
+                           float* lse, void* stream);
+
+/*
+ * GSA gated aggregation (Speed3R section 2.1; Italian summary section 2):
+ *   g = sigmoid(Q[t,h] . w_gate[h]^T + b_gate[h]) in (0,1)^2,
+ *   O[t,h] = g0 * o_cmp[t,h] + g1 * o_slc[t,h].
+ * w_gate: [H, 2, d] fp32, b_gate: [H, 2] fp32 (device). o may alias o_cmp or o_slc.
+ */
+sga_status gsa_gate(const sga_geom* geom, const void* q, const void* o_cmp,
+                    const void* o_slc, const float* w_gate, const float* b_gate,
+                    void* o, void* stream);
+
+/*
+ * AVGGT compaction (AVGGT section 2.2): for every frame, its special tokens and
+ * its patches with r % stride_h == 0 and c % stride_w == 0 (copied exactly),
+ * and -- when any patch is dropped -- one mean K / mean V over the dropped
+ * patches.
+ * Layout of c_k (and c_v): the kept part [N*mk, H, d] (frame-major; per frame
+ * the specials, then the kept patches in row-major grid order), followed when
+ * any patch is dropped by the mean part [N, H, d] (frame f's mean at row N*mk+f).
+ * mk = S + ceil(gh/sh) * ceil(gw/sw). Rows: N*(mk + has_mean), in geom->dtype.
+ */
+sga_status sga_compact(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
+                       const void* k, const void* v, void* c_k, void* c_v, void* stream);
+
+/*
+ * AVGGT subsampled global attention (AVGGT section 2.2): every query is kept;
+ * a query of frame f attends to every token of frame f and to the compacted
+ * set of every other frame (sga_compact). mode 1 is the frame-attention
+ * conversion of the early layers (no workspace needed). With
+ * mean_log_count == 1 the mean token's logit gets log(#dropped) added.
+ * ws: holds the compacted set (sga_compact layout), c_k in the first half and
+ * c_v in the second; its size comes from
+ * sga_workspace_size(geom, SGA_OP_SUBSAMPLED, stride_h, stride_w, &bytes).
+ */
+sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
+                                  int32_t mode, int32_t mean_log_count, const void* q,
+                                  const void* k, const void* v, void* o, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+enum { SGA_OP_SUBSAMPLED = 1 };
+
+/* Workspace bytes an operation needs (0 if none). */
+sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
+                              int32_t param1, size_t* bytes);
+
+/* Thread-local description of the last non-OK status of this thread. */
+const char* sga_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t sga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGA_H */

@@ -99,36 +99,29 @@ def attend_union(q, parts):
 
 
 def head_map(fn, n_heads: int, workers: Optional[int] = None):
-    """Run ``fn(h)`` for every head; in forked worker processes when asked.
+    """Run ``fn(h)`` for every head, on a pool of threads when asked.
 
-    Parallelism only splits independent heads; the arithmetic of ``fn`` is
-    unchanged. ``workers`` defaults to $ORACLE_WORKERS or 1.
+    Parallelism only splits independent heads (NumPy releases the interpreter
+    lock inside its array kernels); the arithmetic of ``fn`` is unchanged.
+    ``workers`` defaults to $ORACLE_WORKERS or 1. BLAS runs single-threaded
+    inside the pool.
     """
     if workers is None:
         workers = int(os.environ.get("ORACLE_WORKERS", "1"))
     if workers <= 1 or n_heads == 1:
         return [fn(h) for h in range(n_heads)]
-    import multiprocessing as mp
-    global _HEAD_FN
-    _HEAD_FN = fn
-    ctx = mp.get_context("fork")
-    with ctx.Pool(min(workers, n_heads), initializer=_limit_threads) as pool:
-        return pool.map(_call_head_fn, range(n_heads))
-
-
-_HEAD_FN = None
-
-
-def _limit_threads():
+    from concurrent.futures import ThreadPoolExecutor
     try:
         from threadpoolctl import threadpool_limits
-        threadpool_limits(1)
+        limit = threadpool_limits(1)
     except Exception:  # pragma: no cover
-        pass
-
-
-def _call_head_fn(h):
-    return _HEAD_FN(h)
+        limit = None
+    try:
+        with ThreadPoolExecutor(max_workers=min(workers, n_heads)) as ex:
+            return list(ex.map(fn, range(n_heads)))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
 
 
 def _rows(rows, T):
@@ -277,7 +270,7 @@ def block_scores(q_blk, k_cmp):
     return np.einsum("bhd,jhd->hbj", qb, kc) / math.sqrt(d)
 
 
-def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64):
+def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None):
     """Top-K pooled blocks per (head, query block) from the compressed scores
     ([Speed3R-ja] section 2.1, selection branch, first bullet; [Speed3R-it]
     section 2, "Ramo di Selezione"). Order: larger score first, ties to the
@@ -292,11 +285,12 @@ def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64):
         raise ValueError("top_k must lie in [1, number of pooled keys]")
     idx = np.empty((H, n, top_k), dtype=np.int32)
     ranked = np.full((H, n, top_k + 1), -np.inf)
-    for h in range(H):
+    m = min(top_k + 1, nk)
+
+    def one_head(h):
         kh = kc[:, h, :]
         for a in range(0, n, chunk):
             s = (qb[a:a + chunk, h, :] @ kh.T) / math.sqrt(d)
-            m = min(top_k + 1, nk)
             # every key ranked within the first m scores at least the m-th largest
             thr = np.partition(s, nk - m, axis=1)[:, nk - m]
             for i in range(s.shape[0]):
@@ -305,6 +299,8 @@ def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64):
                 order = sorted(cand.tolist(), key=lambda j: (-row[j], j))
                 idx[h, a + i] = np.sort(np.array(order[:top_k], dtype=np.int32))
                 ranked[h, a + i, :m] = row[order[:m]]
+
+    head_map(one_head, H, workers)
     return idx, ranked
 
 
@@ -384,12 +380,12 @@ def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
         owner[members] = bi
     need = np.unique(owner[rows])
     q_blk = pooled_queries(q, geom, block, blocks=need)
-    idx_need, ranked = select_topk(q_blk, k_cmp, top_k)
+    idx_need, ranked = select_topk(q_blk, k_cmp, top_k, workers=workers)
     H = q.shape[1]
     idx_full = np.zeros((H, len(qbt), top_k), dtype=np.int32)
     idx_full[:, need] = idx_need
     o_slc = fine_attention(q, k, v, geom, block, idx_full, rows=rows,
-                           keep_special=keep_special)
+                           keep_special=keep_special, workers=workers)
     o = gate(np.asarray(q[rows]), o_cmp, o_slc, w, b)
     return {"k_cmp": k_cmp, "v_cmp": v_cmp, "o_cmp": o_cmp, "blocks": need,
             "q_blk": q_blk, "idx": idx_need, "ranked": ranked, "o_slc": o_slc, "o": o}

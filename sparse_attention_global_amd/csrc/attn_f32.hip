@@ -1,0 +1,93 @@
+// fp32 attention of the forms the bf16 flash kernel serves (dense/compressed,
+// frame, AVGGT subsampled), for fp32 layers: one thread per (query, head),
+// exact online softmax (expf), every product and sum in fp32. The key set and
+// its order follow the same definitions as the bf16 kernel.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sga {
+namespace {
+
+struct F32Args {
+  const float* q;
+  const float* k;
+  const float* v;
+  const float* ck;
+  const float* cv;
+  float* o;
+  float* lse;
+  Geom g;
+  long long n_keys;
+  int mode;
+  int mk;
+  int has_mean;
+  float mean_bias;  // natural-log units
+};
+
+__global__ __launch_bounds__(64) void flash_f32_kernel(F32Args A) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  if (t >= A.g.T) return;
+  const long long rs = (long long)A.g.n_heads * kHeadDim;
+  const long long hoff = (long long)h * kHeadDim;
+  const int f = (int)(t / A.g.L);
+  float qv[kHeadDim], acc[kHeadDim];
+  const float* qp = A.q + t * rs + hoff;
+  for (int e = 0; e < kHeadDim; ++e) { qv[e] = qp[e] * 0.125f; acc[e] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  auto visit = [&](const float* kp, const float* vp, float bias) {
+    float s = bias;
+    for (int e = 0; e < kHeadDim; ++e) s = fmaf(qv[e], kp[e], s);
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);
+    const float pe = expf(s - m_new);
+    for (int e = 0; e < kHeadDim; ++e) acc[e] = fmaf(acc[e], alpha, pe * vp[e]);
+    l = l * alpha + pe;
+    m = m_new;
+  };
+  if (A.mode == FLASH_GLOBAL) {
+    for (long long u = 0; u < A.n_keys; ++u) visit(A.k + u * rs + hoff, A.v + u * rs + hoff, 0.f);
+  } else {
+    const long long f0 = (long long)f * A.g.L;
+    for (long long u = f0; u < f0 + A.g.L; ++u) visit(A.k + u * rs + hoff, A.v + u * rs + hoff, 0.f);
+    if (A.mode == FLASH_SUBSAMPLED) {
+      for (long long r = 0; r < (long long)A.g.n_frames * A.mk; ++r) {
+        if (r / A.mk == f) continue;
+        visit(A.ck + r * rs + hoff, A.cv + r * rs + hoff, 0.f);
+      }
+      if (A.has_mean)
+        for (int g2 = 0; g2 < A.g.n_frames; ++g2) {
+          if (g2 == f) continue;
+          const long long r = (long long)A.g.n_frames * A.mk + g2;
+          visit(A.ck + r * rs + hoff, A.cv + r * rs + hoff, A.mean_bias);
+        }
+    }
+  }
+  float* op = A.o + t * rs + hoff;
+  for (int e = 0; e < kHeadDim; ++e) op[e] = acc[e] / l;
+  if (A.lse) A.lse[t * A.g.n_heads + h] = m + logf(l);
+}
+
+}  // namespace
+
+hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream) {
+  F32Args A{};
+  A.q = static_cast<const float*>(p.q);
+  A.k = static_cast<const float*>(p.k);
+  A.v = static_cast<const float*>(p.v);
+  A.ck = static_cast<const float*>(p.ck);
+  A.cv = static_cast<const float*>(p.cv);
+  A.o = static_cast<float*>(p.o);
+  A.lse = p.lse;
+  A.g = p.g;
+  A.n_keys = p.n_keys;
+  A.mode = p.mode;
+  A.mk = p.mk;
+  A.has_mean = p.has_mean;
+  A.mean_bias = p.mean_bias2 * 0.6931471805599453f;
+  dim3 grid((unsigned)((p.g.T + 63) / 64), (unsigned)p.g.n_heads);
+  hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(64), 0, stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace sga

@@ -1,0 +1,282 @@
+// C ABI of the library (include/sga.h): host-side validation, then dispatch to
+// the kernel launchers. Nothing is enqueued unless every check passes; no C++
+// exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/sga.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sga_status fail(sga_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sga_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SGA_OK;
+  return fail(SGA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr long long kMaxRows = 0x7fffffffLL;  // token and pooled-row counts fit int32
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+  do {                                                                              \
+    if ((p) == nullptr) return fail(SGA_ERR_INVALID_ARG, "%s must not be null", #p); \
+    if (!aligned16(p)) return fail(SGA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p); \
+  } while (0)
+
+#define REQUIRE_OPT_PTR(p)                                                          \
+  do {                                                                              \
+    if ((p) != nullptr && !aligned16(p))                                            \
+      return fail(SGA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p);            \
+  } while (0)
+
+// Validate a geometry and derive the kernels' view of it.
+sga_status make_geom(const sga_geom* in, sga::Geom* g) {
+  if (in == nullptr) return fail(SGA_ERR_INVALID_ARG, "geom must not be null");
+  if (in->n_frames < 1 || in->grid_h < 1 || in->grid_w < 1 || in->n_heads < 1)
+    return fail(SGA_ERR_INVALID_ARG, "n_frames, grid_h, grid_w and n_heads must be >= 1");
+  if (in->n_special < 0 || in->n_special > 16)
+    return fail(SGA_ERR_INVALID_ARG, "n_special must lie in [0, 16]");
+  if (in->head_dim != 64) return fail(SGA_ERR_UNSUPPORTED, "head_dim %d: only 64 is supported", in->head_dim);
+  if (in->dtype != SGA_BF16 && in->dtype != SGA_F32)
+    return fail(SGA_ERR_INVALID_ARG, "dtype %d is neither SGA_BF16 nor SGA_F32", in->dtype);
+  const long long L = (long long)in->n_special + (long long)in->grid_h * in->grid_w;
+  const long long T = L * in->n_frames;
+  if (L > kMaxRows || T > kMaxRows) return fail(SGA_ERR_INVALID_ARG, "token count exceeds 2^31 - 1");
+  if (T * in->n_heads > (1LL << 40)) return fail(SGA_ERR_INVALID_ARG, "T * n_heads too large");
+  g->n_frames = in->n_frames;
+  g->n_special = in->n_special;
+  g->grid_h = in->grid_h;
+  g->grid_w = in->grid_w;
+  g->n_heads = in->n_heads;
+  g->L = (int)L;
+  g->T = T;
+  g->nbh = (in->grid_h + 3) / 4;
+  g->nbw = (in->grid_w + 3) / 4;
+  g->nb = g->nbh * g->nbw;
+  g->nqb = g->nb + (in->n_special > 0 ? 1 : 0);
+  if ((long long)g->nqb * in->n_frames > kMaxRows)
+    return fail(SGA_ERR_INVALID_ARG, "pooled block count exceeds 2^31 - 1");
+  return SGA_OK;
+}
+
+sga_status check_block(int32_t block) {
+  if (block != 4) return fail(SGA_ERR_UNSUPPORTED, "block %d: only 4x4 pooling is supported", block);
+  return SGA_OK;
+}
+
+sga_status check_topk(const sga::Geom& g, int32_t top_k) {
+  const long long n_cand = (long long)g.n_frames * g.nb;
+  if (top_k < 1 || top_k > n_cand || top_k > 128)
+    return fail(SGA_ERR_INVALID_ARG, "top_k %d must lie in [1, min(N*nb = %lld, 128)]", top_k, n_cand);
+  return SGA_OK;
+}
+
+// Rows per frame of the compacted set (kept part) and whether a mean row exists.
+void compact_shape(const sga::Geom& g, int s_h, int s_w, int* mk, int* has_mean, int* n_drop) {
+  const int kh = (g.grid_h + s_h - 1) / s_h, kw = (g.grid_w + s_w - 1) / s_w;
+  *mk = g.n_special + kh * kw;
+  *n_drop = g.grid_h * g.grid_w - kh * kw;
+  *has_mean = *n_drop > 0 ? 1 : 0;
+}
+
+size_t elt_size(const sga_geom* g) { return g->dtype == SGA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k, const void* v,
+                             int64_t n_keys, int32_t frame_local, void* o, float* lse,
+                             void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  REQUIRE_OPT_PTR(lse);
+  if (frame_local != 0 && frame_local != 1) return fail(SGA_ERR_INVALID_ARG, "frame_local must be 0 or 1");
+  if (n_keys < 0 || n_keys > kMaxRows) return fail(SGA_ERR_INVALID_ARG, "n_keys %lld out of range", (long long)n_keys);
+  if (frame_local && n_keys != 0)
+    return fail(SGA_ERR_INVALID_ARG, "frame_local attention takes its keys from the frame: n_keys must be 0");
+  sga::FlashLaunch p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.g = g;
+  p.n_keys = n_keys == 0 ? g.T : n_keys;
+  p.mode = frame_local ? sga::FLASH_FRAME : sga::FLASH_GLOBAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = geom->dtype == SGA_BF16 ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s);
+  return from_hip(e, "dense_global_attn launch");
+}
+
+sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, const void* k,
+                        const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
+                        float* q_blk_f32, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(k_cmp);
+  REQUIRE_PTR(v_cmp);
+  REQUIRE_OPT_PTR(k_cmp_f32);
+  REQUIRE_OPT_PTR(q_blk_f32);
+  if (q_blk_f32 != nullptr) REQUIRE_PTR(q);
+  return from_hip(sga::launch_gsa_pool(g, geom->dtype == SGA_BF16, q, k, v, k_cmp, v_cmp, k_cmp_f32,
+                                       q_blk_f32, static_cast<hipStream_t>(stream)),
+                  "gsa_compress launch");
+}
+
+sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                           const float* k_cmp_f32, int32_t top_k, int32_t* idx, float* score,
+                           void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  if (sga_status st = check_topk(g, top_k)) return st;
+  REQUIRE_PTR(q_blk_f32);
+  REQUIRE_PTR(k_cmp_f32);
+  REQUIRE_PTR(idx);
+  REQUIRE_OPT_PTR(score);
+  return from_hip(sga::launch_gsa_topk(g, q_blk_f32, k_cmp_f32, top_k, idx, score,
+                                       static_cast<hipStream_t>(stream)),
+                  "gsa_select_topk launch");
+}
+
+sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
+                           const void* v, const int32_t* idx, int32_t top_k, int32_t keep_special,
+                           void* o_slc, float* lse, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  if (sga_status st = check_topk(g, top_k)) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(idx);
+  REQUIRE_PTR(o_slc);
+  REQUIRE_OPT_PTR(lse);
+  if (keep_special != 0 && keep_special != 1) return fail(SGA_ERR_INVALID_ARG, "keep_special must be 0 or 1");
+  return from_hip(sga::launch_gsa_fine(g, geom->dtype == SGA_BF16, q, k, v, idx, top_k, keep_special,
+                                       o_slc, lse, static_cast<hipStream_t>(stream)),
+                  "gsa_sparse_attn launch");
+}
+
+sga_status gsa_gate(const sga_geom* geom, const void* q, const void* o_cmp, const void* o_slc,
+                    const float* w_gate, const float* b_gate, void* o, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(o_cmp);
+  REQUIRE_PTR(o_slc);
+  REQUIRE_PTR(w_gate);
+  if (b_gate == nullptr) return fail(SGA_ERR_INVALID_ARG, "b_gate must not be null");
+  REQUIRE_PTR(o);
+  return from_hip(sga::launch_gsa_gate(g, geom->dtype == SGA_BF16, q, o_cmp, o_slc, w_gate, b_gate, o,
+                                       static_cast<hipStream_t>(stream)),
+                  "gsa_gate launch");
+}
+
+sga_status sga_compact(const sga_geom* geom, int32_t stride_h, int32_t stride_w, const void* k,
+                       const void* v, void* c_k, void* c_v, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (stride_h < 1 || stride_w < 1) return fail(SGA_ERR_INVALID_ARG, "strides must be >= 1");
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(c_k);
+  REQUIRE_PTR(c_v);
+  return from_hip(sga::launch_sga_compact(g, geom->dtype == SGA_BF16, stride_h, stride_w, k, v, c_k, c_v,
+                                          static_cast<hipStream_t>(stream)),
+                  "sga_compact launch");
+}
+
+sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, int32_t param1,
+                              size_t* bytes) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (bytes == nullptr) return fail(SGA_ERR_INVALID_ARG, "bytes must not be null");
+  if (op != SGA_OP_SUBSAMPLED) return fail(SGA_ERR_INVALID_ARG, "unknown op %d", op);
+  if (param0 < 1 || param1 < 1) return fail(SGA_ERR_INVALID_ARG, "strides must be >= 1");
+  int mk, has_mean, n_drop;
+  compact_shape(g, param0, param1, &mk, &has_mean, &n_drop);
+  const size_t rows = (size_t)g.n_frames * (size_t)(mk + has_mean);
+  const size_t half = rows * (size_t)g.n_heads * 64 * elt_size(geom);
+  *bytes = 2 * ((half + 255) / 256) * 256;
+  return SGA_OK;
+}
+
+sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
+                                  int32_t mode, int32_t mean_log_count, const void* q,
+                                  const void* k, const void* v, void* o, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o);
+  if (mode != 0 && mode != 1) return fail(SGA_ERR_INVALID_ARG, "mode must be 0 (subsampled) or 1 (frame)");
+  if (mean_log_count != 0 && mean_log_count != 1)
+    return fail(SGA_ERR_INVALID_ARG, "mean_log_count must be 0 or 1");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = geom->dtype == SGA_BF16;
+  sga::FlashLaunch p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.g = g;
+  if (mode == 1) {
+    p.mode = sga::FLASH_FRAME;
+    return from_hip(bf ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s),
+                    "subsampled_global_attn (frame) launch");
+  }
+  if (stride_h < 1 || stride_w < 1) return fail(SGA_ERR_INVALID_ARG, "strides must be >= 1");
+  size_t need = 0;
+  if (sga_status st = sga_workspace_size(geom, SGA_OP_SUBSAMPLED, stride_h, stride_w, &need)) return st;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  int mk, has_mean, n_drop;
+  compact_shape(g, stride_h, stride_w, &mk, &has_mean, &n_drop);
+  unsigned char* c_k = static_cast<unsigned char*>(ws);
+  unsigned char* c_v = c_k + need / 2;
+  if (hipError_t e = sga::launch_sga_compact(g, bf, stride_h, stride_w, k, v, c_k, c_v, s))
+    return from_hip(e, "subsampled_global_attn (compact) launch");
+  p.mode = sga::FLASH_SUBSAMPLED;
+  p.ck = c_k;
+  p.cv = c_v;
+  p.mk = mk;
+  p.has_mean = has_mean;
+  p.mean_bias2 = (mean_log_count && n_drop > 0) ? (float)std::log2((double)n_drop) : 0.f;
+  return from_hip(bf ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s),
+                  "subsampled_global_attn launch");
+}
+
+const char* sga_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sga_version(void) { return 100; }
+
+}  // extern "C"

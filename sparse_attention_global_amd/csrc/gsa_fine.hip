@@ -1,0 +1,261 @@
+// GSA fine attention (Speed3R technical summary section 2.1, selection branch):
+// every query of query block b attends to the in-grid tokens of the pooled
+// blocks selected for b and, when asked, to every special token of every frame
+// (kept whole: the camera tokens of the VGGT adaptation in the Italian summary;
+// the special tokens of AVGGT section 2.2).
+//
+// Work split (bf16): a workgroup of 4 waves owns 8 consecutive query blocks of
+// one head; each wave owns two of them as the 32 MFMA columns (block b0 in
+// columns 0..15, block b0 + 1 in columns 16..31, member m of a 4x4 window at
+// grid offset (m / 4, m % 4); a specials block holds its S tokens).
+//   Phase 1 -- the special tokens are the same keys for every query: they
+//   stream through LDS once per workgroup, double buffered, exactly as in the
+//   dense kernel.
+//   Phase 2 -- each wave gathers its own blocks' selected tokens (top_k windows
+//   x 16 slots, 64 keys = 4 windows per tile) into a private LDS stage; while
+//   one block's keys are processed the other block's 16 columns sit out.
+// Both phases feed the same per-wave online-softmax state, so the result is one
+// softmax over the union of the key sets.
+#include "attn_tile.hpp"
+#include "kernels.hpp"
+
+namespace sga {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 256;
+constexpr int kBlocksPerWG = 2 * kWaves;
+
+struct FineArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const int32_t* idx;  // [H, N*nqb, top_k]
+  bf16* o;
+  float* lse;
+  Geom g;
+  int top_k;
+  int keep_special;
+  int n_wg_per_head;
+  float c;
+};
+
+// Token row of member m (0..15) of query block b, or -1 if the slot is empty.
+__device__ __forceinline__ long long block_member_row(const Geom& g, long long b, int m) {
+  if (b >= (long long)g.n_frames * g.nqb) return -1;
+  const int f = (int)(b / g.nqb), j = (int)(b % g.nqb);
+  const long long base = (long long)f * g.L;
+  if (j == g.nb) return m < g.n_special ? base + m : -1;
+  const int r = 4 * (j / g.nbw) + (m >> 2), c = 4 * (j % g.nbw) + (m & 3);
+  if (r >= g.grid_h || c >= g.grid_w) return -1;
+  return base + g.n_special + (long long)r * g.grid_w + c;
+}
+
+// Token row of slot p (0..15) of pooled window w, or -1 outside the grid (or
+// for a window index outside [0, N*nb), which therefore selects nothing).
+__device__ __forceinline__ long long window_slot_row(const Geom& g, int w, int p) {
+  if (w < 0 || w >= g.n_frames * g.nb) return -1;
+  const int f = w / g.nb, j = w % g.nb;
+  const int r = 4 * (j / g.nbw) + (p >> 2), c = 4 * (j % g.nbw) + (p & 3);
+  if (r >= g.grid_h || c >= g.grid_w) return -1;
+  return (long long)f * g.L + g.n_special + (long long)r * g.grid_w + c;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const Geom& g = A.g;
+  const int h = blockIdx.x / A.n_wg_per_head;
+  const long long wg = blockIdx.x % A.n_wg_per_head;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 31;
+  const int side = li >> 4;  // which of the wave's two blocks owns this column
+  const long long rs = (long long)g.n_heads * kHeadDim;
+  const long long hoff = (long long)h * kHeadDim;
+  const long long n_qb = (long long)g.n_frames * g.nqb;
+  const long long b_wave = wg * kBlocksPerWG + 2 * wave;
+
+  const long long qrow = block_member_row(g, b_wave + side, li & 15);
+  const bool qvalid = qrow >= 0;
+  u32x4 qB[4];
+  load_q_operand(A.q + (qvalid ? qrow : 0) * rs + hoff, qvalid, qB);
+
+  WaveAttnState st;
+  st.init();
+  const float c = A.c;
+
+  // ---- phase 1: all special tokens, shared through LDS ----------------------
+  const long long n_spec = A.keep_special ? (long long)g.n_frames * g.n_special : 0;
+  if (n_spec > 0) {
+    const int ld_key = tid >> 3, ld_chunk = tid & 7;
+    u32x4 kreg[2], vreg[2];
+    auto load_tile = [&](long long u0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const long long u = u0 + ld_key + 32 * i;
+        if (u < n_spec) {
+          const long long row = (u / g.n_special) * g.L + (u % g.n_special);
+          kreg[i] = ld16(A.k + row * rs + hoff + ld_chunk * 8);
+          vreg[i] = ld16(A.v + row * rs + hoff + ld_chunk * 8);
+        } else {
+          kreg[i] = u32x4{0, 0, 0, 0};
+          vreg[i] = u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto store_tile = [&](int stage, long long u0) {
+      unsigned char* sp = smem + stage * kTileStageBytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        tile_store_kv(sp, ld_key + 32 * i, ld_chunk, kreg[i], vreg[i]);
+        if (ld_chunk == 0)
+          tile_bias(sp)[ld_key + 32 * i] = (u0 + ld_key + 32 * i < n_spec) ? 0.f : -INFINITY;
+      }
+    };
+    const long long n_tiles = (n_spec + kTileKeys - 1) / kTileKeys;
+    load_tile(0);
+    store_tile(0, 0);
+    __syncthreads();
+    for (long long it = 0; it < n_tiles; ++it) {
+      const int stage = (int)(it & 1);
+      const long long u0 = it * kTileKeys;
+      const bool more = it + 1 < n_tiles;
+      if (more) load_tile(u0 + kTileKeys);
+      st.step(smem + stage * kTileStageBytes, qB, c, u0 + kTileKeys > n_spec, true);
+      if (more) store_tile(stage ^ 1, u0 + kTileKeys);
+      __syncthreads();
+    }
+  }
+
+  // ---- phase 2: each wave's selected windows, private LDS stage --------------
+  unsigned char* my_stage = smem + wave * kTileStageBytes;
+  const int n_t2 = (A.top_k + 3) / 4;
+  for (int sd = 0; sd < 2; ++sd) {
+    const long long b = b_wave + sd;
+    const bool bvalid = b < n_qb;
+    const int32_t* sel = A.idx + ((long long)h * n_qb + (bvalid ? b : 0)) * A.top_k;
+    for (int t = 0; t < n_t2; ++t) {
+      // lane -> keys (lane >> 3) + 8 i, chunk lane & 7; key u = 16 * window + slot
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 kreg[4], vreg[4];
+        long long rows[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = (lane >> 3) + 8 * (4 * half + i);
+          const int wi = 4 * t + (u >> 4);
+          long long row = -1;
+          if (bvalid && wi < A.top_k) row = window_slot_row(g, sel[wi], u & 15);
+          rows[i] = row;
+          if (row >= 0) {
+            kreg[i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
+            vreg[i] = ld16(A.v + row * rs + hoff + (lane & 7) * 8);
+          } else {
+            kreg[i] = u32x4{0, 0, 0, 0};
+            vreg[i] = u32x4{0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = (lane >> 3) + 8 * (4 * half + i);
+          tile_store_kv(my_stage, u, lane & 7, kreg[i], vreg[i]);
+          if ((lane & 7) == 0) tile_bias(my_stage)[u] = rows[i] >= 0 ? 0.f : -INFINITY;
+        }
+      }
+      __syncthreads();
+      st.step(my_stage, qB, c, true, side == sd && bvalid);
+      __syncthreads();
+    }
+  }
+
+  st.finish(A.o + (qvalid ? qrow : 0) * rs + hoff,
+            A.lse ? A.lse + (qvalid ? qrow : 0) * g.n_heads + h : nullptr, qvalid, c);
+}
+
+// fp32 path: one thread per (query, head), exact online softmax over the same
+// key set (special tokens, then the selected windows' in-grid tokens).
+__global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* __restrict__ q,
+                                                          const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          const int32_t* __restrict__ idx,
+                                                          int top_k, int keep_special,
+                                                          float* __restrict__ o,
+                                                          float* __restrict__ lse) {
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  if (t >= g.T) return;
+  const long long rs = (long long)g.n_heads * kHeadDim;
+  const long long hoff = (long long)h * kHeadDim;
+  const int f = (int)(t / g.L), p = (int)(t % g.L);
+  long long b;
+  if (p < g.n_special) {
+    b = (long long)f * g.nqb + g.nb;
+  } else {
+    const int r = (p - g.n_special) / g.grid_w, cc = (p - g.n_special) % g.grid_w;
+    b = (long long)f * g.nqb + (r >> 2) * g.nbw + (cc >> 2);
+  }
+  float qv[kHeadDim], acc[kHeadDim];
+  const float* qp = q + t * rs + hoff;
+  for (int e = 0; e < kHeadDim; ++e) { qv[e] = qp[e] * 0.125f; acc[e] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  auto visit = [&](long long row) {
+    const float* kp = k + row * rs + hoff;
+    float s = 0.f;
+    for (int e = 0; e < kHeadDim; ++e) s = fmaf(qv[e], kp[e], s);
+    const float m_new = fmaxf(m, s);
+    const float alpha = expf(m - m_new);
+    const float pe = expf(s - m_new);
+    const float* vp = v + row * rs + hoff;
+    for (int e = 0; e < kHeadDim; ++e) acc[e] = fmaf(acc[e], alpha, pe * vp[e]);
+    l = l * alpha + pe;
+    m = m_new;
+  };
+  if (keep_special)
+    for (int ff = 0; ff < g.n_frames; ++ff)
+      for (int s = 0; s < g.n_special; ++s) visit((long long)ff * g.L + s);
+  const long long n_qb = (long long)g.n_frames * g.nqb;
+  const int32_t* sel = idx + ((long long)h * n_qb + b) * top_k;
+  for (int i = 0; i < top_k; ++i)
+    for (int slot = 0; slot < 16; ++slot) {
+      const long long row = window_slot_row(g, sel[i], slot);
+      if (row >= 0) visit(row);
+    }
+  float* op = o + t * rs + hoff;
+  for (int e = 0; e < kHeadDim; ++e) op[e] = acc[e] / l;
+  if (lse) lse[t * g.n_heads + h] = m + logf(l);
+}
+
+}  // namespace
+
+hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
+                           const void* v, const int32_t* idx, int top_k, int keep_special,
+                           void* o, float* lse, hipStream_t stream) {
+  if (!is_bf16) {
+    dim3 grid((unsigned)((g.T + 63) / 64), (unsigned)g.n_heads);
+    hipLaunchKernelGGL(gsa_fine_f32_kernel, grid, dim3(64), 0, stream, g,
+                       static_cast<const float*>(q), static_cast<const float*>(k),
+                       static_cast<const float*>(v), idx, top_k, keep_special,
+                       static_cast<float*>(o), lse);
+    return hipGetLastError();
+  }
+  FineArgs A{};
+  A.q = static_cast<const bf16*>(q);
+  A.k = static_cast<const bf16*>(k);
+  A.v = static_cast<const bf16*>(v);
+  A.idx = idx;
+  A.o = static_cast<bf16*>(o);
+  A.lse = lse;
+  A.g = g;
+  A.top_k = top_k;
+  A.keep_special = keep_special;
+  A.c = kLog2e / sqrtf((float)kHeadDim);
+  const long long n_qb = (long long)g.n_frames * g.nqb;
+  A.n_wg_per_head = (int)((n_qb + kBlocksPerWG - 1) / kBlocksPerWG);
+  const long long grid = (long long)A.n_wg_per_head * g.n_heads;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gsa_fine_bf16_kernel, dim3((unsigned)grid), dim3(kThreads),
+                     kWaves * kTileStageBytes, stream, A);
+  return hipGetLastError();
+}
+
+}  // namespace sga

@@ -1,0 +1,60 @@
+// Host-side launch interface between the C ABI (capi.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns the launch status; argument
+// validation has already happened in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace sga {
+
+enum FlashMode { FLASH_GLOBAL = 0, FLASH_FRAME = 1, FLASH_SUBSAMPLED = 2 };
+
+struct FlashLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* ck;  // SUBSAMPLED: compacted keys (kept part, then mean rows)
+  const void* cv;
+  void* o;
+  float* lse;
+  Geom g;
+  long long n_keys;  // GLOBAL: keys in K/V
+  int mode;          // FlashMode
+  int mk;            // SUBSAMPLED: kept rows per frame
+  int has_mean;      // SUBSAMPLED: one mean row per frame follows the kept part
+  float mean_bias2;  // SUBSAMPLED: log2(#dropped) or 0
+};
+
+// bf16 MFMA flash attention (flash_bf16.hip).
+hipError_t launch_flash_bf16(const FlashLaunch& p, hipStream_t stream);
+// fp32 attention of the same forms (attn_f32.hip).
+hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream);
+
+// GSA pooling (gsa_pool.hip). is_bf16 selects the I/O dtype.
+hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const void* k,
+                           const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
+                           float* q_blk_f32, hipStream_t stream);
+
+// GSA top-K block selection (gsa_topk.hip).
+hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
+                           int32_t* idx, float* score, hipStream_t stream);
+
+// GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32.
+hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
+                           const void* v, const int32_t* idx, int top_k, int keep_special,
+                           void* o, float* lse, hipStream_t stream);
+
+// GSA gate (gsa_gate.hip).
+hipError_t launch_gsa_gate(const Geom& g, bool is_bf16, const void* q, const void* o_cmp,
+                           const void* o_slc, const float* w, const float* b, void* o,
+                           hipStream_t stream);
+
+// AVGGT compaction (sga_compact.hip): kept part [N*mk,H,d], then mean rows [N,H,d].
+hipError_t launch_sga_compact(const Geom& g, bool is_bf16, int s_h, int s_w, const void* k,
+                              const void* v, void* c_k, void* c_v, hipStream_t stream);
+
+}  // namespace sga

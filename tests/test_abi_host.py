@@ -1,0 +1,127 @@
+"""The C-ABI library on the host (no GPU): it loads, exports every function
+include/sga.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_global_amd as sga
+from sparse_attention_global_amd._lib import SgaGeom, library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sga.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = declared_functions()
+    assert set(names) >= {"dense_global_attn", "gsa_compress", "gsa_select_topk", "gsa_sparse_attn",
+                          "gsa_gate", "subsampled_global_attn"}
+    lib = library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(sga.EXPORTS)
+
+
+def test_version():
+    assert library().sga_version() == 100
+
+
+def geom(**kw):
+    base = dict(n_frames=2, n_special=5, grid_h=37, grid_w=37, n_heads=16, head_dim=64, dtype=0)
+    base.update(kw)
+    return SgaGeom(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: calls fail validation first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def last_error():
+    return library().sga_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(head_dim=128), UNSUPPORTED, "head_dim"),
+    (dict(n_frames=0), INVALID, ">= 1"),
+    (dict(n_special=17), INVALID, "n_special"),
+    (dict(dtype=5), INVALID, "dtype"),
+    (dict(grid_h=70000, grid_w=70000), INVALID, "2^31"),
+])
+def test_dense_rejects_bad_geometry(kw, code, msg):
+    g = geom(**kw)
+    st = library().dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, FAKE, None, None)
+    assert st == code
+    assert msg in last_error()
+
+
+def test_dense_rejects_null_and_misaligned():
+    L = library()
+    g = geom()
+    assert L.dense_global_attn(ctypes.byref(g), None, FAKE, FAKE, 0, 0, FAKE, None, None) == INVALID
+    assert "q must not be null" in last_error()
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, MISALIGNED, None, None) == INVALID
+    assert "aligned" in last_error()
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 5, 1, FAKE, None, None) == INVALID
+    assert "frame_local" in last_error()
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, -1, 0, FAKE, None, None) == INVALID
+
+
+def test_gsa_calls_reject_bad_arguments():
+    L = library()
+    g = geom()
+    assert L.gsa_compress(ctypes.byref(g), 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == UNSUPPORTED
+    assert "block" in last_error()
+    # pooled queries requested without q
+    assert L.gsa_compress(ctypes.byref(g), 4, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    nb = 2 * 100
+    for bad_k in (0, nb + 1, 129):
+        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, FAKE, None, None) == INVALID
+        assert "top_k" in last_error()
+    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 2, FAKE, None, None) == INVALID
+    assert "keep_special" in last_error()
+    assert L.gsa_gate(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+
+
+def test_subsampled_rejects_bad_arguments():
+    L = library()
+    g = geom()
+    args = (FAKE, FAKE, FAKE, FAKE)
+    assert L.subsampled_global_attn(ctypes.byref(g), 0, 4, 0, 0, *args, FAKE, 1 << 30, None) == INVALID
+    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 2, 0, *args, FAKE, 1 << 30, None) == INVALID
+    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 3, *args, FAKE, 1 << 30, None) == INVALID
+    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 0, *args, None, 0, None) == WORKSPACE
+    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 0, *args, FAKE, 16, None) == WORKSPACE
+    assert "workspace" in last_error()
+    assert L.sga_compact(ctypes.byref(g), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_workspace_size_matches_compacted_rows():
+    L = library()
+    g = geom(n_frames=256)
+    n = ctypes.c_size_t(0)
+    assert L.sga_workspace_size(ctypes.byref(g), 1, 4, 4, ctypes.byref(n)) == OK
+    # per frame 5 specials + 100 kept + 1 mean = 106 rows, K and V, bf16
+    assert n.value == 2 * 256 * 106 * 16 * 64 * 2
+    assert sga.compact_rows(g, 4, 4) == (105, 1)
+    g1 = geom(n_frames=3, dtype=1)
+    assert L.sga_workspace_size(ctypes.byref(g1), 1, 1, 1, ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * (5 + 37 * 37) * 16 * 64 * 4
+    assert L.sga_workspace_size(ctypes.byref(g1), 7, 1, 1, ctypes.byref(n)) == INVALID
+
+
+def test_python_layer_requires_gpu_tensors():
+    import torch
+    from synth import Geometry
+    gm = Geometry(1, 0, 4, 4, 1, 64, "f32")
+    x = torch.zeros((16, 1, 64))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sga.dense_global_attn(x, x, x, gm)

@@ -1,0 +1,324 @@
+"""HIP library vs the fp64 oracle on the same seeded inputs (needs a gfx950 GPU).
+
+Small cases check every output row; the workload-sized cases check a seeded
+sample of query rows (all heads, all d) plus every intermediate the sampled
+rows depend on.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_global_amd as sga
+from parity import (assert_close, check_topk, decided_blocks, host, oracle_workers)
+from synth import WORKLOADS, Geometry, make_gate, make_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _announce(what):
+    print(f"[case] {what}", flush=True)
+
+
+def _nb(geom):
+    return -(-geom.grid_h // 4) * -(-geom.grid_w // 4)
+
+
+def _nqb(geom):
+    return _nb(geom) + (1 if geom.n_special else 0)
+
+
+def _owner_blocks(geom, rows):
+    """Query block of each token row (windows, then a frame's specials block)."""
+    L = geom.tokens_per_frame
+    out = np.empty(len(rows), dtype=np.int64)
+    nbw = -(-geom.grid_w // 4)
+    for i, t in enumerate(np.asarray(rows)):
+        f, p = divmod(int(t), L)
+        if p < geom.n_special:
+            out[i] = f * _nqb(geom) + _nb(geom)
+        else:
+            r, c = divmod(p - geom.n_special, geom.grid_w)
+            out[i] = f * _nqb(geom) + (r // 4) * nbw + c // 4
+    return out
+
+
+# ---------------------------------------------------------------------------
+# every op, every row, on small geometries
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    pytest.param(WORKLOADS["tiny"].geom, 4, (2, 2), id="tiny-f32"),
+    pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), 5, (4, 4), id="ragged-bf16"),
+    pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), 3, (3, 2), id="ragged-f32"),
+    pytest.param(Geometry(1, 1, 5, 7, 1, 64, "bf16"), 2, (2, 3), id="one-frame-bf16"),
+]
+
+
+@pytest.mark.parametrize("geom,top_k,stride", SMALL)
+def test_small_every_op(geom, top_k, stride):
+    _announce(f"small {geom} top_k={top_k} stride={stride}")
+    dist = "normal" if geom.dtype == "f32" else "scene"
+    q, k, v = make_qkv(geom, seed=11, device=DEV, distribution=dist)
+    w, b = make_gate(geom.n_heads, 64, seed=11, device=DEV)
+    qh, kh, vh = host(q), host(k), host(v)
+    dt = geom.dtype
+    N = geom.n_frames
+
+    # dense + lse, frame
+    o, lse = sga.dense_global_attn(q, k, v, geom, want_lse=True)
+    of = sga.dense_global_attn(q, k, v, geom, frame_local=True)
+    _sync()
+    ro, rlse = oracle.dense_attention(qh, kh, vh, with_lse=True)
+    assert_close(host(o), ro, dt, "dense")
+    assert_close(host(lse), rlse, "f32" if dt == "f32" else "bf16", "dense lse")
+    assert_close(host(of), oracle.frame_attention(qh, kh, vh, geom), dt, "frame")
+
+    # GSA step by step
+    k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
+    _sync()
+    rkc, rvc = oracle.compress(kh, vh, geom, 4)
+    rqb = oracle.pooled_queries(qh, geom, 4)
+    assert_close(host(k_cmp), rkc, dt, "k_cmp")
+    assert_close(host(v_cmp), rvc, dt, "v_cmp")
+    assert_close(host(k32), rkc, "f32", "k_cmp_f32")
+    assert_close(host(q32), rqb, "f32", "q_blk_f32")
+
+    o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * _nb(geom))
+    _sync()
+    r_cmp = oracle.compressed_attention(qh, rkc, rvc)
+    assert_close(host(o_cmp), r_cmp, dt, "o_cmp")
+
+    idx, score = sga.gsa_select_topk(q32, k32, geom, top_k, want_score=True)
+    _sync()
+    ridx, ranked = oracle.select_topk(rqb, rkc, top_k)
+    check_topk(host(idx).astype(np.int64), ridx, ranked, rqb, rkc, "top-K")
+    idx_h, score_h = host(idx).astype(np.int64), host(score)
+    for h in range(geom.n_heads):
+        for bb in range(idx_h.shape[1]):
+            s = rkc[idx_h[h, bb], h, :] @ rqb[bb, h, :] / 8.0
+            assert np.max(np.abs(score_h[h, bb] - s)) < 1e-4
+
+    # fine branch on the oracle's index sets (same input both sides)
+    idx_in = torch.from_numpy(ridx).to(DEV)
+    o_slc, lse_slc = sga.gsa_sparse_attn(q, k, v, idx_in, geom, top_k, want_lse=True)
+    o_slc0 = sga.gsa_sparse_attn(q, k, v, idx_in, geom, top_k, keep_special=False)
+    _sync()
+    r_slc = oracle.fine_attention(qh, kh, vh, geom, 4, ridx)
+    assert_close(host(o_slc), r_slc, dt, "o_slc")
+    assert_close(host(o_slc0), oracle.fine_attention(qh, kh, vh, geom, 4, ridx, keep_special=False),
+                 dt, "o_slc (no specials)")
+
+    # gate on shared inputs
+    o_g = sga.gsa_gate(q, o_cmp, o_slc, w, b, geom)
+    _sync()
+    assert_close(host(o_g), oracle.gate(qh, host(o_cmp), host(o_slc), host(w), host(b)), dt, "gate")
+
+    # the whole layer, on rows whose blocks are decided in every head
+    out = sga.gsa_layer(q, k, v, w, b, geom, top_k)
+    _sync()
+    ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), top_k)
+    dec = decided_blocks(ref["ranked"], top_k).all(axis=0)
+    owner = _owner_blocks(geom, np.arange(geom.n_tokens))
+    pos = {bb: i for i, bb in enumerate(ref["blocks"])}
+    rows = np.array([t for t in range(geom.n_tokens) if dec[pos[owner[t]]]])
+    assert len(rows) > 0.5 * geom.n_tokens
+    assert_close(host(out)[rows], ref["o"][rows], dt, "gsa layer")
+
+    # subsampled: compaction, attention, log-count variant, frame mode
+    sh, sw = stride
+    c_k, c_v = sga.sga_compact(k, v, geom, sh, sw)
+    _sync()
+    rck, rcv = oracle.sga_compact(kh, vh, geom, sh, sw)
+    mk, has_mean = sga.compact_rows(geom, sh, sw)
+    m = mk + has_mean
+    for f in range(N):
+        assert np.array_equal(host(c_k)[f * mk:(f + 1) * mk], rck[f * m:f * m + mk])
+        assert np.array_equal(host(c_v)[f * mk:(f + 1) * mk], rcv[f * m:f * m + mk])
+    if has_mean:
+        assert_close(host(c_k)[N * mk:], rck[m - 1::m], dt, "mean keys")
+        assert_close(host(c_v)[N * mk:], rcv[m - 1::m], dt, "mean values")
+    o_s = sga.subsampled_global_attn(q, k, v, geom, sh, sw)
+    o_sl = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mean_log_count=True)
+    o_sf = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=1)
+    _sync()
+    assert_close(host(o_s), oracle.subsampled_attention(qh, kh, vh, geom, sh, sw), dt, "subsampled")
+    assert_close(host(o_sl), oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, mean_log_count=True),
+                 dt, "subsampled log-count")
+    assert_close(host(o_sf), oracle.frame_attention(qh, kh, vh, geom), dt, "subsampled frame mode")
+
+
+def test_invariants_on_gpu():
+    """The pages' reductions hold on the GPU path too: K = all blocks with the
+    gate forced to the fine branch is dense; stride 1x1 is dense."""
+    geom = Geometry(2, 5, 8, 12, 2, 64, "bf16")
+    _announce(f"invariants {geom}")
+    q, k, v = make_qkv(geom, seed=3, device=DEV, distribution="scene")
+    nb = geom.n_frames * _nb(geom)
+    w = torch.zeros((2, 2, 64), device=DEV)
+    b = torch.tensor([[-float("inf"), float("inf")]] * 2, device=DEV)
+    o_gsa = sga.gsa_layer(q, k, v, w, b, geom, nb)
+    o_s1 = sga.subsampled_global_attn(q, k, v, geom, 1, 1)
+    o_d = sga.dense_global_attn(q, k, v, geom)
+    _sync()
+    ref = oracle.dense_attention(host(q), host(k), host(v))
+    assert_close(host(o_gsa), ref, "bf16", "gsa(K=all, fine gate) vs dense oracle")
+    assert_close(host(o_s1), ref, "bf16", "stride 1 vs dense oracle")
+    assert_close(host(o_d), ref, "bf16", "dense")
+
+
+def test_topk_planted_winners():
+    """Designed pooled scores with known, separated winners: block b's pooled
+    query is the unit vector of coordinate c_b, so only keys of class c_b score,
+    by their planted magnitudes (spaced 0.01 apart, i.e. 1.25e-3 in score)."""
+    geom = Geometry(128, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"planted top-K {geom}")
+    N, H = geom.n_frames, geom.n_heads
+    nk, nq = N * _nb(geom), N * _nqb(geom)
+    rng = np.random.default_rng(5)
+    cls = np.arange(nk) % 64
+    k32 = rng.standard_normal((nk, H, 64)) * 1e-6
+    mag = np.empty(nk)
+    for c in range(64):
+        members = np.nonzero(cls == c)[0]
+        mag[members] = 1.0 + 0.01 * rng.permutation(len(members))
+    for h in range(H):
+        k32[np.arange(nk), h, cls] += mag
+    qc = rng.integers(0, 64, size=(nq, H))
+    q32 = np.zeros((nq, H, 64))
+    for h in range(H):
+        q32[np.arange(nq), h, qc[:, h]] = 1.0
+    idx = sga.gsa_select_topk(torch.tensor(q32, dtype=torch.float32, device=DEV),
+                              torch.tensor(k32, dtype=torch.float32, device=DEV), geom, 16)
+    _sync()
+    got = host(idx).astype(np.int64)
+    for h in range(H):
+        for bb in range(0, nq, 97):
+            members = np.nonzero(cls == qc[bb, h])[0]
+            want = np.sort(members[np.argsort(-mag[members], kind="stable")[:16]])
+            assert np.array_equal(got[h, bb], want), (h, bb)
+
+
+def test_deterministic():
+    geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
+    _announce(f"determinism {geom}")
+    q, k, v = make_qkv(geom, seed=9, device=DEV, distribution="scene")
+    w, b = make_gate(geom.n_heads, 64, seed=9, device=DEV)
+    a = sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True)
+    c = sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True)
+    d1 = sga.dense_global_attn(q, k, v, geom)
+    d2 = sga.dense_global_attn(q, k, v, geom)
+    s1 = sga.subsampled_global_attn(q, k, v, geom, 4, 4)
+    s2 = sga.subsampled_global_attn(q, k, v, geom, 4, 4)
+    _sync()
+    for key in a:
+        assert torch.equal(a[key], c[key]), key
+    assert torch.equal(d1, d2)
+    assert torch.equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# workload-sized cases: seeded row samples
+# ---------------------------------------------------------------------------
+
+def _workload_inputs(name, seed=1):
+    wl = WORKLOADS[name]
+    geom = wl.geom
+    q, k, v = make_qkv(geom, seed=seed, device=DEV, distribution=wl.distribution)
+    return wl, geom, q, k, v
+
+
+def _plant_probes(q, k, geom, n_probe, seed):
+    """Give n_probe query rows one sharply matching key each, far away in the
+    token order, so that an indexing slip changes their output completely."""
+    rng = np.random.default_rng(seed)
+    T, H = geom.n_tokens, geom.n_heads
+    probes = rng.choice(T, n_probe, replace=False)
+    targets = rng.choice(T, n_probe, replace=False)
+    u = torch.randn((n_probe, H, 64), generator=torch.Generator().manual_seed(seed))
+    u = u / u.norm(dim=-1, keepdim=True) * 15.5
+    u = u.to(q.dtype).to(q.device)
+    k[torch.from_numpy(targets).to(q.device)] = u
+    q[torch.from_numpy(probes).to(q.device)] = u
+    return np.sort(probes)
+
+
+@pytest.mark.timeout(900)
+def test_dense32():
+    wl, geom, q, k, v = _workload_inputs("dense32")
+    probes = _plant_probes(q, k, geom, 64, seed=2)
+    rows = np.union1d(sample_rows(geom.n_tokens, wl.check_rows, seed=1).numpy(), probes)
+    _announce(f"dense32 dense+frame, {len(rows)} rows")
+    o = sga.dense_global_attn(q, k, v, geom)
+    of = sga.dense_global_attn(q, k, v, geom, frame_local=True)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    W = oracle_workers()
+    assert_close(host(o)[rows], oracle.dense_attention(qh, kh, vh, rows=rows, workers=W), "bf16",
+                 "dense32 dense")
+    assert_close(host(of)[rows], oracle.frame_attention(qh, kh, vh, geom, rows=rows), "bf16",
+                 "dense32 frame")
+
+
+def _gsa_check(name, rows_cap=None):
+    wl, geom, q, k, v = _workload_inputs(name)
+    w, b = make_gate(geom.n_heads, 64, seed=1, device=DEV)
+    rows = sample_rows(geom.n_tokens, rows_cap or wl.check_rows, seed=1).numpy()
+    _announce(f"{name} GSA layer, {len(rows)} rows")
+    out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    W = oracle_workers()
+    ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), wl.top_k, rows=rows, workers=W)
+    assert_close(host(out["k_cmp"]), ref["k_cmp"], "bf16", f"{name} k_cmp")
+    assert_close(host(out["v_cmp"]), ref["v_cmp"], "bf16", f"{name} v_cmp")
+    assert_close(host(out["k_cmp_f32"]), ref["k_cmp"], "f32", f"{name} k_cmp_f32")
+    assert_close(host(out["q_blk_f32"])[ref["blocks"]], ref["q_blk"], "f32", f"{name} q_blk_f32")
+    assert_close(host(out["o_cmp"])[rows], ref["o_cmp"], "bf16", f"{name} o_cmp")
+    idx = host(out["idx"]).astype(np.int64)[:, ref["blocks"]]
+    check_topk(idx, ref["idx"], ref["ranked"], ref["q_blk"], ref["k_cmp"], f"{name} top-K")
+    # rows whose query block is decided in every head see identical index sets
+    dec = decided_blocks(ref["ranked"], wl.top_k).all(axis=0)
+    owner = _owner_blocks(geom, rows)
+    pos = {bb: i for i, bb in enumerate(ref["blocks"])}
+    keep = np.array([dec[pos[o]] for o in owner])
+    print(f"[parity] {name}: {keep.mean() * 100:.1f}% of sampled rows fully decided", flush=True)
+    assert keep.sum() > 0
+    assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", f"{name} o_slc")
+    assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer")
+
+
+@pytest.mark.timeout(900)
+def test_gsa128():
+    _gsa_check("gsa128")
+
+
+def _sga_check(name, rows_cap=None):
+    wl, geom, q, k, v = _workload_inputs(name)
+    rows = sample_rows(geom.n_tokens, rows_cap or wl.check_rows, seed=1).numpy()
+    _announce(f"{name} subsampled + frame, {len(rows)} rows")
+    sh, sw = wl.stride
+    o = sga.subsampled_global_attn(q, k, v, geom, sh, sw)
+    of = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=1)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    W = oracle_workers()
+    assert_close(host(o)[rows], oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, rows=rows,
+                                                            workers=W), "bf16", f"{name} subsampled")
+    assert_close(host(of)[rows], oracle.frame_attention(qh, kh, vh, geom, rows=rows), "bf16",
+                 f"{name} frame")
+
+
+@pytest.mark.timeout(900)
+def test_sga256():
+    _sga_check("sga256")
