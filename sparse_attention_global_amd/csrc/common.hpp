@@ -74,6 +74,18 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// l + the sum of the 8 bf16 values packed in w (v_dot2 with (1, 1)). The lanes
+// are named explicitly: indexing the vector inside an unrolled loop and
+// bit-casting the element to bf16x2 miscompiles (every term read lane 0).
+__device__ __forceinline__ float sum_bf16x8(const u32x4& w, float l) {
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)w.x), ones, l, false);
+  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)w.y), ones, l, false);
+  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)w.z), ones, l, false);
+  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, (uint32_t)w.w), ones, l, false);
+  return l;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------

@@ -139,24 +139,36 @@ __global__ __launch_bounds__(kThreads, 2) void flash_bf16_kernel(FlashArgs A) {
 
   WaveAttnState st;
   st.init();
+  TileLaneOffsets off;
+  off.init();
 
   // loader: keys (tid >> 3) and (tid >> 3) + 32 of a tile, 16-byte chunk tid & 7
   const int ld_key = tid >> 3, ld_chunk = tid & 7;
   u32x4 kreg[2], vreg[2];
   float breg[2];
+  // GLOBAL and FRAME keys are contiguous rows: walk a pointer; SUBSAMPLED maps
+  // every key through its segment
+  const long long key_base = (MODE == MODE_FRAME) ? (long long)f * A.g.L : 0;
   auto load_tile = [&](long long u0) {
+    const bool full = u0 + kTileKeys <= nk;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const long long u = u0 + ld_key + 32 * i;
-      const KeyRow kr = key_row<MODE>(A, hoff, f, nk, u);
-      const bool ok = u < nk;
-      kreg[i] = ok ? ld16(kr.k + ld_chunk * 8) : u32x4{0, 0, 0, 0};
-      vreg[i] = ok ? ld16(kr.v + ld_chunk * 8) : u32x4{0, 0, 0, 0};
-      breg[i] = kr.bias;
+      if (MODE != MODE_SUBSAMPLED && full) {
+        const long long o = (key_base + u) * rs + hoff + ld_chunk * 8;
+        kreg[i] = ld16(A.k + o);
+        vreg[i] = ld16(A.v + o);
+        breg[i] = 0.f;
+      } else {
+        const KeyRow kr = key_row<MODE>(A, hoff, f, nk, u);
+        const bool ok = u < nk;
+        kreg[i] = ok ? ld16(kr.k + ld_chunk * 8) : u32x4{0, 0, 0, 0};
+        vreg[i] = ok ? ld16(kr.v + ld_chunk * 8) : u32x4{0, 0, 0, 0};
+        breg[i] = kr.bias;
+      }
     }
   };
-  auto store_tile = [&](int stage) {
-    unsigned char* sp = smem + stage * kTileStageBytes;
+  auto store_tile = [&](unsigned char* sp) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       tile_store_kv(sp, ld_key + 32 * i, ld_chunk, kreg[i], vreg[i]);
@@ -164,18 +176,30 @@ __global__ __launch_bounds__(kThreads, 2) void flash_bf16_kernel(FlashArgs A) {
     }
   };
 
+  unsigned char* const stage0 = smem;
+  unsigned char* const stage1 = smem + kTileStageBytes;
   const long long n_tiles = (nk + kTileKeys - 1) / kTileKeys;
   load_tile(0);
-  store_tile(0);
+  store_tile(stage0);
   __syncthreads();
-  for (long long it = 0; it < n_tiles; ++it) {
-    const int stage = (int)(it & 1);
-    const long long u0 = it * kTileKeys;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(u0 + kTileKeys);
-    st.step(smem + stage * kTileStageBytes, qB, c, u0 + kTileKeys > bias_from, true);
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
+  // two tiles per iteration so each stage's LDS offsets are immediates
+  for (long long it = 0; it < n_tiles; it += 2) {
+    {
+      const long long u0 = it * kTileKeys;
+      const bool more = it + 1 < n_tiles;
+      if (more) load_tile(u0 + kTileKeys);
+      st.step(stage0, off, qB, c, u0 + kTileKeys > bias_from, true);
+      if (more) store_tile(stage1);
+      __syncthreads();
+    }
+    if (it + 1 < n_tiles) {
+      const long long u0 = (it + 1) * kTileKeys;
+      const bool more = it + 2 < n_tiles;
+      if (more) load_tile(u0 + kTileKeys);
+      st.step(stage1, off, qB, c, u0 + kTileKeys > bias_from, true);
+      if (more) store_tile(stage0);
+      __syncthreads();
+    }
   }
   st.finish(A.o + qrow * rs + hoff, A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr, qvalid, c);
 }

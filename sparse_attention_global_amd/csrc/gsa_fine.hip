@@ -82,6 +82,8 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
 
   WaveAttnState st;
   st.init();
+  TileLaneOffsets off;
+  off.init();
   const float c = A.c;
 
   // ---- phase 1: all special tokens, shared through LDS ----------------------
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
       const long long u0 = it * kTileKeys;
       const bool more = it + 1 < n_tiles;
       if (more) load_tile(u0 + kTileKeys);
-      st.step(smem + stage * kTileStageBytes, qB, c, u0 + kTileKeys > n_spec, true);
+      st.step(smem + stage * kTileStageBytes, off, qB, c, u0 + kTileKeys > n_spec, true);
       if (more) store_tile(stage ^ 1, u0 + kTileKeys);
       __syncthreads();
     }
@@ -137,12 +139,12 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
     for (int t = 0; t < n_t2; ++t) {
       // lane -> keys (lane >> 3) + 8 i, chunk lane & 7; key u = 16 * window + slot
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 kreg[4], vreg[4];
-        long long rows[4];
+      for (int part = 0; part < 4; ++part) {
+        u32x4 kreg[2], vreg[2];
+        long long rows[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int u = (lane >> 3) + 8 * (4 * half + i);
+        for (int i = 0; i < 2; ++i) {
+          const int u = (lane >> 3) + 8 * (2 * part + i);
           const int wi = 4 * t + (u >> 4);
           long long row = -1;
           if (bvalid && wi < A.top_k) row = window_slot_row(g, sel[wi], u & 15);
@@ -156,14 +158,14 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
           }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int u = (lane >> 3) + 8 * (4 * half + i);
+        for (int i = 0; i < 2; ++i) {
+          const int u = (lane >> 3) + 8 * (2 * part + i);
           tile_store_kv(my_stage, u, lane & 7, kreg[i], vreg[i]);
           if ((lane & 7) == 0) tile_bias(my_stage)[u] = rows[i] >= 0 ? 0.f : -INFINITY;
         }
       }
       __syncthreads();
-      st.step(my_stage, qB, c, true, side == sd && bvalid);
+      st.step(my_stage, off, qB, c, true, side == sd && bvalid);
       __syncthreads();
     }
   }
