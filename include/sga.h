@@ -65,10 +65,14 @@ typedef struct {
  *   (Speed3R section 2.1): k, v = the pooled K/V of gsa_compress and
  *   n_keys = N * nb.
  * lse (nullable): [T, H] fp32, natural-log log-sum-exp of the scaled logits.
+ * ws: scratch of sga_workspace_size(geom, SGA_OP_DENSE, n_keys, frame_local)
+ *   bytes (bf16: the values staged transposed for the matrix cores; fp32: none,
+ *   ws may be NULL).
  */
 sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
                              const void* v, int64_t n_keys, int32_t frame_local,
-                             void* o, float* lse, void* stream);
+                             void* o, float* lse, void* ws, size_t ws_bytes,
+                             void* stream);
 
 /*
  * GSA compression (Speed3R section 2.1, compression branch): block x block
@@ -143,20 +147,22 @@ sga_status sga_compact(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
  * AVGGT subsampled global attention (AVGGT section 2.2): every query is kept;
  * a query of frame f attends to every token of frame f and to the compacted
  * set of every other frame (sga_compact). mode 1 is the frame-attention
- * conversion of the early layers (no workspace needed). With
+ * conversion of the early layers. With
  * mean_log_count == 1 the mean token's logit gets log(#dropped) added.
- * ws: holds the compacted set (sga_compact layout), c_k in the first half and
- * c_v in the second; its size comes from
- * sga_workspace_size(geom, SGA_OP_SUBSAMPLED, stride_h, stride_w, &bytes).
+ * ws: sga_workspace_size(geom, SGA_OP_SUBSAMPLED, stride_h, stride_w, &bytes)
+ * bytes: the compacted keys and values (sga_compact layout, each region
+ * rounded up to 256 bytes), then for bf16 the values staged transposed.
  */
 sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
                                   int32_t mode, int32_t mean_log_count, const void* q,
                                   const void* k, const void* v, void* o, void* ws,
                                   size_t ws_bytes, void* stream);
 
-enum { SGA_OP_SUBSAMPLED = 1 };
+enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2 };
 
-/* Workspace bytes an operation needs (0 if none). */
+/* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
+ * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
+ * stride_h, stride_w (covers both modes). */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

@@ -19,6 +19,7 @@ _lib = None
 
 SGA_BF16, SGA_F32 = 0, 1
 SGA_OP_SUBSAMPLED = 1
+SGA_OP_DENSE = 2
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_select_topk", "gsa_sparse_attn", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
@@ -43,7 +44,7 @@ def library() -> ctypes.CDLL:
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     G = ctypes.POINTER(SgaGeom)
     sig = {
-        "dense_global_attn": [G, P, P, P, I64, I32, P, P, P],
+        "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
         "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
         "gsa_select_topk": [G, I32, P, P, I32, P, P, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P],
@@ -113,8 +114,26 @@ def pooled_shape(geom, block: int = 4):
 
 # ---------------------------------------------------------------------------
 
+def dense_workspace_bytes(geom, dtype_code: int, n_keys: int = 0, frame_local: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    g = make_geom(geom, dtype_code)
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_DENSE, n_keys, int(frame_local),
+                                        ctypes.byref(n)), "sga_workspace_size")
+    return n.value
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return ws
+    if ws is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace of {nbytes} bytes needed")
+    return ws
+
+
 def dense_global_attn(q, k, v, geom, n_keys: int = 0, frame_local: bool = False,
-                      want_lse: bool = False):
+                      want_lse: bool = False, ws=None):
     """Dense (or frame-local, or pooled-key) attention; see include/sga.h."""
     T, H, d = tokens(geom), geom.n_heads, 64
     _need(q, "q", T, H, d)
@@ -123,10 +142,13 @@ def dense_global_attn(q, k, v, geom, n_keys: int = 0, frame_local: bool = False,
     _need(v, "v", nk, H, d, q.dtype)
     o = torch.empty_like(q)
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if want_lse else None
-    g = make_geom(geom, _dtype_code(q))
+    code = _dtype_code(q)
+    ws = _workspace(dense_workspace_bytes(geom, code, n_keys, frame_local), q.device, ws)
+    g = make_geom(geom, code)
     _check(library().dense_global_attn(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), n_keys,
-                                       int(frame_local), _ptr(o), _ptr(lse), _stream(q)),
-           "dense_global_attn")
+                                       int(frame_local), _ptr(o), _ptr(lse), _ptr(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream(q)), "dense_global_attn")
     return (o, lse) if want_lse else o
 
 
@@ -241,9 +263,8 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
     _need(k, "k", T, H, d, q.dtype)
     _need(v, "v", T, H, d, q.dtype)
     code = _dtype_code(q)
-    nbytes = 0 if mode == 1 else workspace_bytes(geom, s_h, s_w, code)
-    if ws is None and nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    nbytes = workspace_bytes(geom, max(s_h, 1), max(s_w, 1), code)
+    ws = _workspace(nbytes, q.device, ws)
     o = torch.empty_like(q)
     g = make_geom(geom, code)
     _check(library().subsampled_global_attn(ctypes.byref(g), s_h, s_w, mode, int(mean_log_count),

@@ -9,18 +9,19 @@
 // factor) and P^T feeds the MFMA B operand straight from its score registers.
 //
 // LDS stage layout (kTileStageBytes):
-//   K tile  64 keys x 128 B; 16-byte chunk c of key row r lives at chunk c ^ (r & 7),
-//           so the 16-byte operand reads of 8 consecutive lanes (8 rows, one
-//           logical chunk) cover all 32 banks.
-//   V tile  64 keys x 128 B, row-major like K; chunk c of row r lives at
-//           c ^ ((r & 3) << 1). The PV operand is read with the gfx950 LDS
-//           transpose load (ds_read_b64_tr_b16): inside a group of 16 lanes,
-//           lane j names an 8-byte piece M[j][0..3] and lane i receives
-//           M[4e + i/4][i % 4] for e = 0..3. Pointing lane j at
-//           V[key0 + j/4][d0 + 4 (j % 4)] hands lane i the column d0 + i for the
-//           four keys key0 .. key0 + 3 -- the A-operand layout of V^T. The
-//           swizzle keeps those 4 rows x 32 bytes on 32 distinct banks.
-//   bias    64 floats added (log2 units) to the tile's logits when asked
+//   K tile    64 keys x 128 B; 16-byte chunk c of key row r lives at chunk
+//             c ^ (r & 7), so the 16-byte operand reads of 8 consecutive lanes
+//             (8 rows, one logical chunk) cover all 32 banks.
+//   V^T tile  64 d-rows x 128 B of keys. Within every 16-key group the key
+//             offset 8a + 4hh + r sits at column 8hh + 4a + r, so one 16-byte
+//             read returns exactly the 8 keys of a lane's MFMA B slots; chunk x
+//             of row d lives at x ^ ((d & 7) ^ ((d >> 3) & 7)). The loader
+//             transposes in registers: a thread holding two consecutive keys'
+//             8-value chunks packs (key, key+1) pairs per d with v_perm and
+//             writes them as dwords (the pair is adjacent in the column order).
+//             16-byte LDS reads run about 3x the bandwidth of the gfx950 LDS
+//             transpose read, which is why V is transposed on the way in.
+//   bias      64 floats added (log2 units) to the tile's logits when asked
 #pragma once
 
 #include "common.hpp"
@@ -36,26 +37,38 @@ constexpr float kLazyRescaleLog2 = 8.0f;
 __device__ __forceinline__ int tile_k_off(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
-__device__ __forceinline__ int tile_v_off(int row, int chunk) {
-  return kTileKBytes + row * 128 + ((chunk ^ ((row & 3) << 1)) << 4);
+__device__ __forceinline__ int tile_vt_off(int d, int pos) {
+  const int swz = (d & 7) ^ ((d >> 3) & 7);
+  return kTileKBytes + d * 128 + (((pos >> 3) ^ swz) << 4) + ((pos & 7) << 1);
+}
+// Column of key offset u (0..63) inside a V^T row: within each 16-key group the
+// offset 8a + 4hh + r moves to 8hh + 4a + r.
+__device__ __forceinline__ int tile_vt_pos(int u) {
+  const int o = u & 15;
+  const int a = o >> 3, hh = (o >> 2) & 1, r = o & 3;
+  return (u & ~15) | (hh << 3) | (a << 2) | r;
 }
 
-// Write one 16-byte chunk (8 d-values) of key u's K and V rows into a stage.
-__device__ __forceinline__ void tile_store_kv(unsigned char* stage, int u, int chunk,
-                                             const u32x4& kw, const u32x4& vw) {
-  st16(stage + tile_k_off(u, chunk), kw);
-  st16(stage + tile_v_off(u, chunk), vw);
+// Write the 16-byte chunk `chunk` (8 d-values) of keys u and u + 1 (u even)
+// into a stage: K rows as they are, V transposed as (u, u + 1) dword pairs.
+__device__ __forceinline__ void tile_store_kv_pair(unsigned char* stage, int u, int chunk,
+                                                  const u32x4& ka, const u32x4& kb,
+                                                  const u32x4& va, const u32x4& vb) {
+  st16(stage + tile_k_off(u, chunk), ka);
+  st16(stage + tile_k_off(u + 1, chunk), kb);
+  const int pos = tile_vt_pos(u);  // pos(u + 1) = pos(u) + 1
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = chunk * 8 + 2 * j;
+    // perm(x, y, sel) picks bytes of {x: 4..7, y: 0..3}
+    const uint32_t lo = __builtin_amdgcn_perm(vb[j], va[j], 0x05040100u);  // (va.lo, vb.lo)
+    const uint32_t hi = __builtin_amdgcn_perm(vb[j], va[j], 0x07060302u);  // (va.hi, vb.hi)
+    *reinterpret_cast<uint32_t*>(stage + tile_vt_off(d, pos)) = lo;
+    *reinterpret_cast<uint32_t*>(stage + tile_vt_off(d + 1, pos)) = hi;
+  }
 }
 __device__ __forceinline__ float* tile_bias(unsigned char* stage) {
   return reinterpret_cast<float*>(stage + kTileKBytes + kTileVBytes);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-// Transposing 8-byte LDS read (see the layout note above).
-__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* p) {
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, r);
 }
 
 // Q^T operand of a wave: lane l loads d = 16 ks + 8 (l/32) .. +8 of its query row.
@@ -71,20 +84,19 @@ __device__ __forceinline__ void load_q_operand(const bf16* qrow_ptr, bool valid,
 // computed once per kernel so the tile loop does no address arithmetic.
 struct TileLaneOffsets {
   uint32_t k[4];  // K rows li (+32 kb as an immediate), chunk 2 ks + hh
-  uint32_t v[2];  // V rows 4 hh + (l % 16) / 4, columns 32 db + 16 ((l / 16) % 2) + 4 (l % 4);
-                  // the key block 32 kb + 16 mm + 8 r adds as an immediate
+  uint32_t v[8];  // V^T row 32 db + li, keys 32 kb + 16 mm + 8 hh; index 4 db + 2 kb + mm
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5, li = lane & 31;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) k[ks] = (uint32_t)tile_k_off(li, 2 * ks + hh);
-    const int j = lane & 15, gd = (lane >> 4) & 1;
-    const int row = 4 * hh + (j >> 2);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const int byte = 2 * (db * 32 + 16 * gd + 4 * (j & 3));
-      v[db] = (uint32_t)(tile_v_off(row, byte >> 4) + (byte & 15));
-    }
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+          v[4 * db + 2 * kb + mm] = (uint32_t)tile_vt_off(db * 32 + li, kb * 32 + 16 * mm + 8 * hh);
   }
 };
 
@@ -100,23 +112,14 @@ struct WaveAttnState {
     l = 0.f;
   }
 
-  // One 64-key tile. c = log2(e)/sqrt(d). use_bias adds the stage's bias row;
-  // inactive lanes (a query not attending these keys) skip the tile.
-  // Operand reads are issued in batches ahead of the MFMAs that consume them;
-  // the V^T operands are requested before the softmax so their LDS latency
-  // hides behind it.
-  __device__ __forceinline__ void step(const unsigned char* stage, const TileLaneOffsets& off,
-                                       const u32x4 qB[4], float c, bool use_bias, bool active) {
-    const int lane = threadIdx.x & 63;
-    const int hh = lane >> 5;
-    const float* bs = reinterpret_cast<const float*>(stage + kTileKBytes + kTileVBytes);
-
+  // Scores of one 64-key tile: S^T = K Q^T for two 32-key blocks.
+  __device__ __forceinline__ void scores(const unsigned char* stage, const TileLaneOffsets& off,
+                                         const u32x4 qB[4], f32x16 s[2]) const {
     u32x4 ka[2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
-    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 acc;
@@ -126,20 +129,20 @@ struct WaveAttnState {
       for (int ks = 0; ks < 4; ++ks) acc = mfma32(ka[kb][ks], qB[ks], acc);
       s[kb] = acc;
     }
-    // V^T operands: slots 0..3 and 4..7 of MFMA (db, kb, mm) are the keys
-    // 32 kb + 16 mm + {0, 8} + 4 hh + 0..3 of column 32 db + (l % 32)
+  }
+
+  // Softmax of a tile's scores and O^T += V^T P^T with the tile's values.
+  // c = log2(e)/sqrt(d); use_bias adds the stage's bias row; inactive lanes
+  // (a query not attending these keys) skip the tile. The V^T operands are
+  // requested before the softmax so their LDS latency hides behind it.
+  __device__ __forceinline__ void consume(f32x16 s[2], const unsigned char* stage,
+                                          const TileLaneOffsets& off, float c, bool use_bias,
+                                          bool active) {
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5;
+    const float* bs = reinterpret_cast<const float*>(stage + kTileKBytes + kTileVBytes);
     u32x4 va[8];
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const unsigned char* p = stage + off.v[db] + (kb * 32 + 16 * mm) * 128;
-          const u32x2 lo = lds_read_tr16(p);
-          const u32x2 hi = lds_read_tr16(p + 8 * 128);
-          va[4 * db + 2 * kb + mm] = u32x4{lo.x, lo.y, hi.x, hi.y};
-        }
+    read_v(stage, off, va);
 
     if (use_bias) {
       const float inv_c = 1.f / c;
@@ -197,6 +200,99 @@ struct WaveAttnState {
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
           oacc[db] = mfma32(va[4 * db + 2 * kb + mm], pB[kb][mm], oacc[db]);
+  }
+
+  // ---- pieces of the software-pipelined tile step (all lanes active) --------
+
+  // V^T operands of a tile: MFMA (db, kb, mm) reads d-row 32 db + (l % 32),
+  // keys 32 kb + 16 mm + 8 hh .. +8 of the permuted column order.
+  __device__ __forceinline__ void read_v(const unsigned char* stage, const TileLaneOffsets& off,
+                                         u32x4 va[8]) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) va[i] = ld16(stage + off.v[i]);
+  }
+
+  __device__ __forceinline__ void add_bias(f32x16 s[2], const unsigned char* stage, float c) const {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const float* bs = reinterpret_cast<const float*>(stage + kTileKBytes + kTileVBytes);
+    const float inv_c = 1.f / c;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + kb * 32 + 8 * g4 + 4 * hh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[kb][4 * g4 + r] = fmaf(b4[r], inv_c, s[kb][4 * g4 + r]);
+      }
+  }
+
+  // Running max of the tile's rows; rescales O and l when the lazy threshold trips.
+  __device__ __forceinline__ void update_max(const f32x16 s[2], float c) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m, mx);
+    if (__any((m_new - m) * c > kLazyRescaleLog2)) {
+      const float alpha = fast_exp2((m - m_new) * c);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
+    }
+  }
+
+  // Branch-free block: P = exp2(S c - m c) of this tile, row sums, O^T += V^T P^T,
+  // and the next tile's scores s_next = K' Q^T, interleaved MFMA / VALU.
+  __device__ __forceinline__ void exp_pv_scores(f32x16 s[2], const u32x4 va[8], float c,
+                                                const u32x4 ka[2][4], const u32x4 qB[4],
+                                                f32x16 s_next[2]) {
+    const float mc = m * c;  // every lane has seen a finite key by now
+    u32x4 pB[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32(ka[kb][ks], qB[ks], acc);
+      s_next[kb] = acc;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[kb][8 * mm + i], c, -mc));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pB[kb][mm][jj] = pack_bf16x2(p[2 * jj], p[2 * jj + 1]);
+        l = sum_bf16x8(pB[kb][mm], l);
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+          oacc[db] = mfma32(va[4 * db + 2 * kb + mm], pB[kb][mm], oacc[db]);
+    // interleave: each MFMA followed by a run of VALU work
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // six VALU / transcendental
+    }
+  }
+
+  // One whole 64-key tile: scores then softmax + PV.
+  __device__ __forceinline__ void step(const unsigned char* stage, const TileLaneOffsets& off,
+                                       const u32x4 qB[4], float c, bool use_bias, bool active) {
+    f32x16 s[2];
+    scores(stage, off, qB, s);
+    consume(s, stage, off, c, use_bias, active);
   }
 
   // Normalise and store query (l % 32)'s row (if valid); lse in natural-log units.

@@ -98,13 +98,43 @@ void compact_shape(const sga::Geom& g, int s_h, int s_w, int* mk, int* has_mean,
 
 size_t elt_size(const sga_geom* g) { return g->dtype == SGA_BF16 ? 2 : 4; }
 
+// FlashLaunch of a dense_global_attn call (validated geometry and keys).
+sga::FlashLaunch dense_launch(const sga::Geom& g, int64_t n_keys, int32_t frame_local) {
+  sga::FlashLaunch p{};
+  p.g = g;
+  p.n_keys = n_keys == 0 ? g.T : n_keys;
+  p.mode = frame_local ? sga::FLASH_FRAME : sga::FLASH_GLOBAL;
+  return p;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace layout of subsampled_global_attn (bf16 and fp32): compacted keys,
+// compacted values, then (bf16) the attention kernel's V^T staging.
+void subsampled_layout(const sga_geom* geom, const sga::Geom& g, int s_h, int s_w,
+                              size_t* half, size_t* flash) {
+  int mk, has_mean, n_drop;
+  compact_shape(g, s_h, s_w, &mk, &has_mean, &n_drop);
+  const size_t rows = (size_t)g.n_frames * (size_t)(mk + has_mean);
+  *half = round256(rows * (size_t)g.n_heads * 64 * elt_size(geom));
+  *flash = 0;
+  if (geom->dtype == SGA_BF16) {
+    sga::FlashLaunch p{};
+    p.g = g;
+    p.mode = sga::FLASH_SUBSAMPLED;
+    p.mk = mk;
+    p.has_mean = has_mean;
+    *flash = round256(sga::flash_bf16_workspace(p));
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
 sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k, const void* v,
-                             int64_t n_keys, int32_t frame_local, void* o, float* lse,
-                             void* stream) {
+                             int64_t n_keys, int32_t frame_local, void* o, float* lse, void* ws,
+                             size_t ws_bytes, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   REQUIRE_PTR(q);
@@ -116,18 +146,19 @@ sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
   if (n_keys < 0 || n_keys > kMaxRows) return fail(SGA_ERR_INVALID_ARG, "n_keys %lld out of range", (long long)n_keys);
   if (frame_local && n_keys != 0)
     return fail(SGA_ERR_INVALID_ARG, "frame_local attention takes its keys from the frame: n_keys must be 0");
-  sga::FlashLaunch p{};
+  sga::FlashLaunch p = dense_launch(g, n_keys, frame_local);
   p.q = q;
   p.k = k;
   p.v = v;
   p.o = o;
   p.lse = lse;
-  p.g = g;
-  p.n_keys = n_keys == 0 ? g.T : n_keys;
-  p.mode = frame_local ? sga::FLASH_FRAME : sga::FLASH_GLOBAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = geom->dtype == SGA_BF16 ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s);
-  return from_hip(e, "dense_global_attn launch");
+  if (geom->dtype != SGA_BF16) return from_hip(sga::launch_flash_f32(p, s), "dense_global_attn launch");
+  const size_t need = sga::flash_bf16_workspace(p);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  return from_hip(sga::launch_flash_bf16(p, ws, s), "dense_global_attn launch");
 }
 
 sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, const void* k,
@@ -217,13 +248,17 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (bytes == nullptr) return fail(SGA_ERR_INVALID_ARG, "bytes must not be null");
+  if (op == SGA_OP_DENSE) {
+    if (param0 < 0 || (param1 != 0 && param1 != 1) || (param1 && param0 != 0))
+      return fail(SGA_ERR_INVALID_ARG, "dense workspace: n_keys >= 0, frame_local 0/1 (n_keys 0 if 1)");
+    *bytes = geom->dtype == SGA_BF16 ? sga::flash_bf16_workspace(dense_launch(g, param0, param1)) : 0;
+    return SGA_OK;
+  }
   if (op != SGA_OP_SUBSAMPLED) return fail(SGA_ERR_INVALID_ARG, "unknown op %d", op);
   if (param0 < 1 || param1 < 1) return fail(SGA_ERR_INVALID_ARG, "strides must be >= 1");
-  int mk, has_mean, n_drop;
-  compact_shape(g, param0, param1, &mk, &has_mean, &n_drop);
-  const size_t rows = (size_t)g.n_frames * (size_t)(mk + has_mean);
-  const size_t half = rows * (size_t)g.n_heads * 64 * elt_size(geom);
-  *bytes = 2 * ((half + 255) / 256) * 256;
+  size_t half, flash;
+  subsampled_layout(geom, g, param0, param1, &half, &flash);
+  *bytes = 2 * half + flash;
   return SGA_OK;
 }
 
@@ -248,10 +283,14 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   p.v = v;
   p.o = o;
   p.g = g;
-  if (mode == 1) {
+  if (mode == 1) {  // frame attention: the V^T staging is a prefix of the workspace
     p.mode = sga::FLASH_FRAME;
-    return from_hip(bf ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s),
-                    "subsampled_global_attn (frame) launch");
+    if (!bf) return from_hip(sga::launch_flash_f32(p, s), "subsampled_global_attn (frame) launch");
+    const size_t need = sga::flash_bf16_workspace(p);
+    if (ws == nullptr || ws_bytes < need)
+      return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+    if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+    return from_hip(sga::launch_flash_bf16(p, ws, s), "subsampled_global_attn (frame) launch");
   }
   if (stride_h < 1 || stride_w < 1) return fail(SGA_ERR_INVALID_ARG, "strides must be >= 1");
   size_t need = 0;
@@ -261,8 +300,10 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
   int mk, has_mean, n_drop;
   compact_shape(g, stride_h, stride_w, &mk, &has_mean, &n_drop);
+  size_t half, flash;
+  subsampled_layout(geom, g, stride_h, stride_w, &half, &flash);
   unsigned char* c_k = static_cast<unsigned char*>(ws);
-  unsigned char* c_v = c_k + need / 2;
+  unsigned char* c_v = c_k + half;
   if (hipError_t e = sga::launch_sga_compact(g, bf, stride_h, stride_w, k, v, c_k, c_v, s))
     return from_hip(e, "subsampled_global_attn (compact) launch");
   p.mode = sga::FLASH_SUBSAMPLED;
@@ -271,7 +312,7 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   p.mk = mk;
   p.has_mean = has_mean;
   p.mean_bias2 = (mean_log_count && n_drop > 0) ? (float)std::log2((double)n_drop) : 0.f;
-  return from_hip(bf ? sga::launch_flash_bf16(p, s) : sga::launch_flash_f32(p, s),
+  return from_hip(bf ? sga::launch_flash_bf16(p, c_k + 2 * half, s) : sga::launch_flash_f32(p, s),
                   "subsampled_global_attn launch");
 }
 

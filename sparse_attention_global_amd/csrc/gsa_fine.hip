@@ -89,12 +89,12 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
   // ---- phase 1: all special tokens, shared through LDS ----------------------
   const long long n_spec = A.keep_special ? (long long)g.n_frames * g.n_special : 0;
   if (n_spec > 0) {
-    const int ld_key = tid >> 3, ld_chunk = tid & 7;
+    const int ld_key = 2 * (tid >> 3), ld_chunk = tid & 7;
     u32x4 kreg[2], vreg[2];
     auto load_tile = [&](long long u0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const long long u = u0 + ld_key + 32 * i;
+        const long long u = u0 + ld_key + i;
         if (u < n_spec) {
           const long long row = (u / g.n_special) * g.L + (u % g.n_special);
           kreg[i] = ld16(A.k + row * rs + hoff + ld_chunk * 8);
@@ -107,11 +107,10 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
     };
     auto store_tile = [&](int stage, long long u0) {
       unsigned char* sp = smem + stage * kTileStageBytes;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        tile_store_kv(sp, ld_key + 32 * i, ld_chunk, kreg[i], vreg[i]);
-        if (ld_chunk == 0)
-          tile_bias(sp)[ld_key + 32 * i] = (u0 + ld_key + 32 * i < n_spec) ? 0.f : -INFINITY;
+      tile_store_kv_pair(sp, ld_key, ld_chunk, kreg[0], kreg[1], vreg[0], vreg[1]);
+      if (ld_chunk == 0) {
+        tile_bias(sp)[ld_key] = (u0 + ld_key < n_spec) ? 0.f : -INFINITY;
+        tile_bias(sp)[ld_key + 1] = (u0 + ld_key + 1 < n_spec) ? 0.f : -INFINITY;
       }
     };
     const long long n_tiles = (n_spec + kTileKeys - 1) / kTileKeys;
@@ -137,17 +136,17 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
     const bool bvalid = b < n_qb;
     const int32_t* sel = A.idx + ((long long)h * n_qb + (bvalid ? b : 0)) * A.top_k;
     for (int t = 0; t < n_t2; ++t) {
-      // lane -> keys (lane >> 3) + 8 i, chunk lane & 7; key u = 16 * window + slot
+      // lane -> key pair 2 ((lane >> 3) + 8 part), chunk lane & 7; key u = 16 * window + slot
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
+        const int u = 2 * ((lane >> 3) + 8 * part);
         u32x4 kreg[2], vreg[2];
         long long rows[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const int u = (lane >> 3) + 8 * (2 * part + i);
-          const int wi = 4 * t + (u >> 4);
+          const int wi = 4 * t + ((u + i) >> 4);
           long long row = -1;
-          if (bvalid && wi < A.top_k) row = window_slot_row(g, sel[wi], u & 15);
+          if (bvalid && wi < A.top_k) row = window_slot_row(g, sel[wi], (u + i) & 15);
           rows[i] = row;
           if (row >= 0) {
             kreg[i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
@@ -157,11 +156,10 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
             vreg[i] = u32x4{0, 0, 0, 0};
           }
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int u = (lane >> 3) + 8 * (2 * part + i);
-          tile_store_kv(my_stage, u, lane & 7, kreg[i], vreg[i]);
-          if ((lane & 7) == 0) tile_bias(my_stage)[u] = rows[i] >= 0 ? 0.f : -INFINITY;
+        tile_store_kv_pair(my_stage, u, lane & 7, kreg[0], kreg[1], vreg[0], vreg[1]);
+        if ((lane & 7) == 0) {
+          tile_bias(my_stage)[u] = rows[0] >= 0 ? 0.f : -INFINITY;
+          tile_bias(my_stage)[u + 1] = rows[1] >= 0 ? 0.f : -INFINITY;
         }
       }
       __syncthreads();

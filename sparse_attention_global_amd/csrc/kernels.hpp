@@ -18,7 +18,7 @@ struct FlashLaunch {
   const void* k;
   const void* v;
   const void* ck;  // SUBSAMPLED: compacted keys (kept part, then mean rows)
-  const void* cv;
+  const void* cv;  // SUBSAMPLED: compacted values, same rows
   void* o;
   float* lse;
   Geom g;
@@ -29,8 +29,15 @@ struct FlashLaunch {
   float mean_bias2;  // SUBSAMPLED: log2(#dropped) or 0
 };
 
-// bf16 MFMA flash attention (flash_bf16.hip).
-hipError_t launch_flash_bf16(const FlashLaunch& p, hipStream_t stream);
+// bf16 MFMA flash attention (flash_bf16.hip). ws holds the V^T staging of the
+// values (and of the compacted values in SUBSAMPLED mode); its size is
+// flash_bf16_workspace(p).
+size_t flash_bf16_workspace(const FlashLaunch& p);
+hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream);
+// V^T staging (vt_prepare.hip): vt[(h*64 + d)*ld + col] = v[key(col), h, d], keys
+// in segments of seg_len padded to seg_pad columns, MFMA key order in 16-column groups.
+hipError_t launch_vt_prepare(const void* v, int n_heads, long long n_rows, long long seg_len,
+                             long long seg_pad, long long ld, void* vt, hipStream_t stream);
 // fp32 attention of the same forms (attn_f32.hip).
 hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream);
 

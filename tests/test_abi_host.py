@@ -58,7 +58,7 @@ def last_error():
 ])
 def test_dense_rejects_bad_geometry(kw, code, msg):
     g = geom(**kw)
-    st = library().dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, FAKE, None, None)
+    st = library().dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, FAKE, None, FAKE, 1 << 40, None)
     assert st == code
     assert msg in last_error()
 
@@ -66,13 +66,18 @@ def test_dense_rejects_bad_geometry(kw, code, msg):
 def test_dense_rejects_null_and_misaligned():
     L = library()
     g = geom()
-    assert L.dense_global_attn(ctypes.byref(g), None, FAKE, FAKE, 0, 0, FAKE, None, None) == INVALID
+    big = 1 << 40
+    assert L.dense_global_attn(ctypes.byref(g), None, FAKE, FAKE, 0, 0, FAKE, None, FAKE, big, None) == INVALID
     assert "q must not be null" in last_error()
-    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, MISALIGNED, None, None) == INVALID
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, MISALIGNED, None, FAKE, big, None) == INVALID
     assert "aligned" in last_error()
-    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 5, 1, FAKE, None, None) == INVALID
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 5, 1, FAKE, None, FAKE, big, None) == INVALID
     assert "frame_local" in last_error()
-    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, -1, 0, FAKE, None, None) == INVALID
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, -1, 0, FAKE, None, FAKE, big, None) == INVALID
+    # bf16 needs the V^T staging workspace
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, FAKE, None, None, 0, None) == WORKSPACE
+    assert L.dense_global_attn(ctypes.byref(g), FAKE, FAKE, FAKE, 0, 0, FAKE, None, FAKE, 64, None) == WORKSPACE
+    assert "workspace" in last_error()
 
 
 def test_gsa_calls_reject_bad_arguments():
@@ -104,18 +109,36 @@ def test_subsampled_rejects_bad_arguments():
     assert L.sga_compact(ctypes.byref(g), 4, 0, FAKE, FAKE, FAKE, FAKE, None) == INVALID
 
 
-def test_workspace_size_matches_compacted_rows():
-    L = library()
-    g = geom(n_frames=256)
+def _ws(g, op, a, b):
     n = ctypes.c_size_t(0)
-    assert L.sga_workspace_size(ctypes.byref(g), 1, 4, 4, ctypes.byref(n)) == OK
-    # per frame 5 specials + 100 kept + 1 mean = 106 rows, K and V, bf16
-    assert n.value == 2 * 256 * 106 * 16 * 64 * 2
+    st = library().sga_workspace_size(ctypes.byref(g), op, a, b, ctypes.byref(n))
+    return st, n.value
+
+
+def r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_sizes():
+    g = geom(n_frames=256)
+    T = 256 * 1374
+    # dense bf16: V^T staging, keys rounded up to 64 columns, 16 heads x 64 rows of d
+    assert _ws(g, 2, 0, 0) == (OK, 16 * 64 * ((T + 63) // 64 * 64) * 2)
+    assert _ws(g, 2, 25600, 0) == (OK, 16 * 64 * 25600 * 2)
+    # frame mode: every frame padded to 1408 columns
+    assert _ws(g, 2, 0, 1) == (OK, 16 * 64 * 1408 * 256 * 2)
+    assert _ws(g, 2, 5, 1)[0] == INVALID
+    # subsampled: per frame 5 specials + 100 kept + 1 mean = 106 rows of K and V,
+    # then the frame-padded V^T and the V^T of the 27,136 compacted rows
+    half = r256(256 * 106 * 16 * 64 * 2)
+    flash = r256(16 * 64 * 1408 * 256 * 2 + 16 * 64 * ((256 * 106 + 63) // 64 * 64) * 2)
+    assert _ws(g, 1, 4, 4) == (OK, 2 * half + flash)
     assert sga.compact_rows(g, 4, 4) == (105, 1)
+    # fp32 keeps only the compacted set, dense needs nothing
     g1 = geom(n_frames=3, dtype=1)
-    assert L.sga_workspace_size(ctypes.byref(g1), 1, 1, 1, ctypes.byref(n)) == OK
-    assert n.value == 2 * 3 * (5 + 37 * 37) * 16 * 64 * 4
-    assert L.sga_workspace_size(ctypes.byref(g1), 7, 1, 1, ctypes.byref(n)) == INVALID
+    assert _ws(g1, 1, 1, 1) == (OK, 2 * r256(3 * (5 + 37 * 37) * 16 * 64 * 4))
+    assert _ws(g1, 2, 0, 0) == (OK, 0)
+    assert _ws(g1, 7, 1, 1)[0] == INVALID
 
 
 def test_python_layer_requires_gpu_tensors():
