@@ -84,19 +84,23 @@ __device__ __forceinline__ void load_q_operand(const bf16* qrow_ptr, bool valid,
 // computed once per kernel so the tile loop does no address arithmetic.
 struct TileLaneOffsets {
   uint32_t k[4];  // K rows li (+32 kb as an immediate), chunk 2 ks + hh
-  uint32_t v[8];  // V^T row 32 db + li, keys 32 kb + 16 mm + 8 hh; index 4 db + 2 kb + mm
+  // V^T row 32 db + li (+4096 db as an immediate), keys 32 kb + 16 mm + 8 hh:
+  // the swizzled chunk (4 kb + 2 mm + hh) ^ swz(d) depends on kb and db only
+  // through kb ^ db, so four offsets (a = kb ^ db, mm) cover all eight reads
+  uint32_t v[4];
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5, li = lane & 31;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) k[ks] = (uint32_t)tile_k_off(li, 2 * ks + hh);
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-          v[4 * db + 2 * kb + mm] = (uint32_t)tile_vt_off(db * 32 + li, kb * 32 + 16 * mm + 8 * hh);
+      for (int mm = 0; mm < 2; ++mm)  // db = 0, kb = a
+        v[2 * a + mm] = (uint32_t)tile_vt_off(li, a * 32 + 16 * mm + 8 * hh);
+  }
+  __device__ __forceinline__ uint32_t v_off(int db, int kb, int mm) const {
+    return v[2 * (kb ^ db) + mm] + db * 32 * 128;
   }
 };
 
@@ -141,8 +145,6 @@ struct WaveAttnState {
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
     const float* bs = reinterpret_cast<const float*>(stage + kTileKBytes + kTileVBytes);
-    u32x4 va[8];
-    read_v(stage, off, va);
 
     if (use_bias) {
       const float inv_c = 1.f / c;
@@ -199,7 +201,7 @@ struct WaveAttnState {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
-          oacc[db] = mfma32(va[4 * db + 2 * kb + mm], pB[kb][mm], oacc[db]);
+          oacc[db] = mfma32(ld16(stage + off.v_off(db, kb, mm)), pB[kb][mm], oacc[db]);
   }
 
   // ---- pieces of the software-pipelined tile step (all lanes active) --------
@@ -209,7 +211,11 @@ struct WaveAttnState {
   __device__ __forceinline__ void read_v(const unsigned char* stage, const TileLaneOffsets& off,
                                          u32x4 va[8]) const {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) va[i] = ld16(stage + off.v[i]);
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) va[4 * db + 2 * kb + mm] = ld16(stage + off.v_off(db, kb, mm));
   }
 
   __device__ __forceinline__ void add_bias(f32x16 s[2], const unsigned char* stage, float c) const {

@@ -13,10 +13,10 @@
 // The per-tile math (attn_tile.hpp) keeps every per-query quantity inside the
 // lane that owns the query.
 //
-// Data movement: keys stream in tiles of 64 through a ring of four LDS
-// stages. Every K row and every V^T row of a tile moves from HBM/L2 straight
-// into LDS with 16-byte direct loads (global_load_lds_dwordx4) issued three
-// tiles ahead -- no registers, no VALU address work per tile, no LDS write
+// Data movement: keys stream in tiles of 64 through a ring of LDS stages.
+// Every K row and every V^T row of a tile moves from HBM/L2 straight into LDS
+// with 16-byte direct loads (global_load_lds_dwordx4) issued one or two tiles
+// ahead -- no registers, no VALU address work per tile, no LDS write
 // instructions. The swizzled LDS layouts are produced by choosing which
 // 16-byte chunk each lane fetches. V^T comes from a staging pass (vt_prepare)
 // that already holds V transposed in the MFMA operand's key order. A tile is
@@ -38,11 +38,19 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = kWaves * 32;         // 128 queries per workgroup
-constexpr int kStages = 4;                   // LDS ring
-constexpr int kAhead = 3;                    // tiles in flight ahead of the one consumed
 constexpr int kRowsPerWave = 64 / kWaves;    // K rows and V^T rows each wave fetches per tile
 constexpr int kLoadsPerTile = 2 * kRowsPerWave / 8;  // 16-byte direct loads per lane per tile
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
+// Occupancy: the kernel is issue- and latency-bound, so it runs with more
+// resident waves and a shorter LDS ring rather than fewer waves with a deep
+// prefetch (measured on MI355X at 128 frames: 4 stages / 2 waves per SIMD
+// 35.3%, 3 / 3 38.1%, 2 / 4 39.0% of bf16 peak for dense attention; the
+// subsampled form, with more scalar bookkeeping, does best at 3 / 3).
+template <int MODE>
+struct Ring {
+  static constexpr int stages = (MODE == 2) ? 3 : 2;
+  static constexpr int wg_per_cu = (MODE == 2) ? 3 : 4;
+};
 
 enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
 
@@ -95,8 +103,10 @@ __device__ __forceinline__ void wait_and_meet() {
 }
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void flash_bf16_kernel(FlashArgs A) {
+__global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_kernel(FlashArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int kStages = Ring<MODE>::stages;  // LDS ring
+  constexpr int kAhead = kStages - 1;          // tiles in flight ahead of the one consumed
 
   int lid = blockIdx.x;
   if (A.remap) {
@@ -223,14 +233,17 @@ __global__ __launch_bounds__(kThreads, 2) void flash_bf16_kernel(FlashArgs A) {
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
     if (j < n_tiles) issue_tile(j, smem + j * kStageBytes);
-
+  static_assert(kStages >= 2 && kStages <= 4, "ring of 2 to 4 stages");
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   auto body = [&](long long j, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr int refill = (cur + kAhead) % kStages;
     const long long left = n_tiles - 1 - j;  // tiles after j already in flight: min(kAhead-1, left)
     if (left >= kAhead - 1) {
       wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
-    } else if (left == 1) {
+    } else if (kAhead > 2 && left == 1) {
       wait_and_meet<kLoadsPerTile>();
     } else {
       wait_and_meet<0>();
@@ -242,16 +255,15 @@ __global__ __launch_bounds__(kThreads, 2) void flash_bf16_kernel(FlashArgs A) {
     if (needs_mask(j)) apply_mask(j, s);
     st.consume(s, stage, off, c, false, true);
   };
-  static_assert(kAhead == 3 && kStages == 4, "wait counts assume 3 tiles ahead, 4 stages");
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  for (long long j = 0; j < n_tiles; j += 4) {
+  for (long long j = 0; j < n_tiles; j += kStages) {
     body(j, I0{});
     if (j + 1 < n_tiles) body(j + 1, I1{});
-    if (j + 2 < n_tiles) body(j + 2, I2{});
-    if (j + 3 < n_tiles) body(j + 3, I3{});
+    if constexpr (kStages > 2) {
+      if (j + 2 < n_tiles) body(j + 2, std::integral_constant<int, 2>{});
+    }
+    if constexpr (kStages > 3) {
+      if (j + 3 < n_tiles) body(j + 3, std::integral_constant<int, 3>{});
+    }
   }
   st.finish(A.o + qrow * rs + hoff, A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr, qvalid, c);
 }
@@ -316,16 +328,18 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   if (n_logical > 0x7ffffff0LL) return hipErrorInvalidValue;
   A.n_logical = (int)n_logical;
   const int grid = A.remap ? ((A.n_logical + 7) / 8) * 8 : A.n_logical;
-  const size_t lds = kStages * kStageBytes;
   switch (p.mode) {
     case FLASH_GLOBAL:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_GLOBAL>, dim3(grid), dim3(kThreads), lds, stream, A);
+      hipLaunchKernelGGL(flash_bf16_kernel<MODE_GLOBAL>, dim3(grid), dim3(kThreads),
+                         Ring<MODE_GLOBAL>::stages * kStageBytes, stream, A);
       break;
     case FLASH_FRAME:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_FRAME>, dim3(grid), dim3(kThreads), lds, stream, A);
+      hipLaunchKernelGGL(flash_bf16_kernel<MODE_FRAME>, dim3(grid), dim3(kThreads),
+                         Ring<MODE_FRAME>::stages * kStageBytes, stream, A);
       break;
     default:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_SUBSAMPLED>, dim3(grid), dim3(kThreads), lds, stream, A);
+      hipLaunchKernelGGL(flash_bf16_kernel<MODE_SUBSAMPLED>, dim3(grid), dim3(kThreads),
+                         Ring<MODE_SUBSAMPLED>::stages * kStageBytes, stream, A);
       break;
   }
   return hipGetLastError();
