@@ -453,8 +453,8 @@ def subsampled_attention(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 
     def one_head(h):
         o = np.empty((len(rows), d))
-        ckh = np.asarray(ck[:, h, :], np.float64)
-        cvh = np.asarray(cv[:, h, :], np.float64)
+        ckh = np.ascontiguousarray(ck[:, h, :], np.float64)
+        cvh = np.ascontiguousarray(cv[:, h, :], np.float64)
         for a in range(0, len(rows), chunk):
             idx = np.arange(a, min(a + chunk, len(rows)))
             qc = np.asarray(q[rows[idx], h, :], np.float64)
@@ -462,15 +462,18 @@ def subsampled_attention(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
             s_c = (qc @ ckh.T) * scale + bias_c
             for i, f in enumerate(frames[idx]):
                 s_c[i, f * m:(f + 1) * m] = -np.inf  # ... minus the query's own frame
+            # ... plus its own frame whole; one softmax over the union per row
+            s_own = np.empty((len(idx), L))
+            v_own = np.empty((len(idx), L, d))
             for i, f in enumerate(frames[idx]):
                 own = slice(f * L, (f + 1) * L)
-                k_own = np.asarray(k[own, h, :], np.float64)
-                v_own = np.asarray(v[own, h, :], np.float64)
-                s_own = (qc[i] @ k_own.T) * scale  # ... plus its own frame whole
-                mx = max(s_own.max(), s_c[i].max())
-                p_own = np.exp(s_own - mx)
-                p_c = np.exp(s_c[i] - mx)
-                o[idx[i]] = (p_own @ v_own + p_c @ cvh) / (p_own.sum() + p_c.sum())
+                s_own[i] = (np.asarray(k[own, h, :], np.float64) @ qc[i]) * scale
+                v_own[i] = v[own, h, :]
+            mx = np.maximum(s_own.max(axis=1), s_c.max(axis=1))[:, None]
+            p_own = np.exp(s_own - mx)
+            p_c = np.exp(s_c - mx)
+            num = np.einsum("il,ild->id", p_own, v_own) + p_c @ cvh
+            o[idx] = num / (p_own.sum(axis=1) + p_c.sum(axis=1))[:, None]
         return o
 
     return np.stack(head_map(one_head, H, workers), axis=1)
