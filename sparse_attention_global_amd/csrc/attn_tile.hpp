@@ -204,95 +204,6 @@ struct WaveAttnState {
           oacc[db] = mfma32(ld16(stage + off.v_off(db, kb, mm)), pB[kb][mm], oacc[db]);
   }
 
-  // ---- pieces of the software-pipelined tile step (all lanes active) --------
-
-  // V^T operands of a tile: MFMA (db, kb, mm) reads d-row 32 db + (l % 32),
-  // keys 32 kb + 16 mm + 8 hh .. +8 of the permuted column order.
-  __device__ __forceinline__ void read_v(const unsigned char* stage, const TileLaneOffsets& off,
-                                         u32x4 va[8]) const {
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) va[4 * db + 2 * kb + mm] = ld16(stage + off.v_off(db, kb, mm));
-  }
-
-  __device__ __forceinline__ void add_bias(f32x16 s[2], const unsigned char* stage, float c) const {
-    const int hh = (threadIdx.x & 63) >> 5;
-    const float* bs = reinterpret_cast<const float*>(stage + kTileKBytes + kTileVBytes);
-    const float inv_c = 1.f / c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 b4 = *reinterpret_cast<const f32x4*>(bs + kb * 32 + 8 * g4 + 4 * hh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[kb][4 * g4 + r] = fmaf(b4[r], inv_c, s[kb][4 * g4 + r]);
-      }
-  }
-
-  // Running max of the tile's rows; rescales O and l when the lazy threshold trips.
-  __device__ __forceinline__ void update_max(const f32x16 s[2], float c) {
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m, mx);
-    if (__any((m_new - m) * c > kLazyRescaleLog2)) {
-      const float alpha = fast_exp2((m - m_new) * c);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { oacc[0][i] *= alpha; oacc[1][i] *= alpha; }
-    }
-  }
-
-  // Branch-free block: P = exp2(S c - m c) of this tile, row sums, O^T += V^T P^T,
-  // and the next tile's scores s_next = K' Q^T, interleaved MFMA / VALU.
-  __device__ __forceinline__ void exp_pv_scores(f32x16 s[2], const u32x4 va[8], float c,
-                                                const u32x4 ka[2][4], const u32x4 qB[4],
-                                                f32x16 s_next[2]) {
-    const float mc = m * c;  // every lane has seen a finite key by now
-    u32x4 pB[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma32(ka[kb][ks], qB[ks], acc);
-      s_next[kb] = acc;
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(s[kb][8 * mm + i], c, -mc));
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pB[kb][mm][jj] = pack_bf16x2(p[2 * jj], p[2 * jj + 1]);
-        l = sum_bf16x8(pB[kb][mm], l);
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-          oacc[db] = mfma32(va[4 * db + 2 * kb + mm], pB[kb][mm], oacc[db]);
-    // interleave: each MFMA followed by a run of VALU work
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);  // six VALU / transcendental
-    }
-  }
-
   // One whole 64-key tile: scores then softmax + PV.
   __device__ __forceinline__ void step(const unsigned char* stage, const TileLaneOffsets& off,
                                        const u32x4 qB[4], float c, bool use_bias, bool active) {
@@ -318,6 +229,96 @@ struct WaveAttnState {
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
     if (lse_ptr != nullptr && hh == 0) *lse_ptr = (m * c + __log2f(l_tot)) * 0.6931471805599453f;
+  }
+};
+
+// Q' operand with the softmax scale folded in: bf16(q * c), nearest-even, so
+// that K Q'^T is the logit in log2 units.
+__device__ __forceinline__ void load_q_operand_scaled(const bf16* qrow_ptr, bool valid, float c,
+                                                      u32x4 qB[4]) {
+  load_q_operand(qrow_ptr, valid, qB);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qB[ks][j] = pack_bf16x2(lo_bf16(qB[ks][j]) * c, hi_bf16(qB[ks][j]) * c);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming softmax against a fixed upper bound (the flash kernel's main pass).
+//
+// With Q' = bf16(q c) the MFMA returns logits S' in log2 units. Every logit of
+// a query is at most b = |q'| max_k |k| (Cauchy-Schwarz), so with the
+// accumulator started at -b (broadcast in `negm`) the MFMA returns S' - b <= 0
+// and each probability is one v_exp: no scaling, subtraction, running maximum
+// or rescaling per score. The normalised result does not depend on the
+// reference; a fixed one only risks underflow when b exceeds the row's true
+// maximum by more than the fp32 exponent range can absorb, which the caller
+// detects from the final sum and then redoes the rows with the exact online
+// softmax (WaveAttnState with c = 1).
+// ---------------------------------------------------------------------------
+struct FlashWaveState {
+  f32x16 oacc[2];  // O^T for d 0..31 and 32..63 of query (l % 32)
+  f32x16 negm;     // -b in every element
+  float m;         // the reference b, log2 units
+  float l;         // this half-wave's share of sum exp2(S' - b)
+
+  __device__ __forceinline__ void init(float bound) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { oacc[0][i] = 0.f; oacc[1][i] = 0.f; negm[i] = -bound; }
+    m = bound;
+    l = 0.f;
+  }
+
+  // Half kb (keys 32 kb .. 32 kb + 31) of a staged tile. mask(kb, s) applies the
+  // tile's key mask and logit bias (log2 units) when `masked`.
+  template <class MaskFn>
+  __device__ __forceinline__ void half(const unsigned char* stage, const TileLaneOffsets& off,
+                                       int kb, const u32x4 qB[4], bool masked, MaskFn&& mask) {
+    u32x4 ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
+    f32x16 s = mfma32(ka[0], qB[0], negm);
+#pragma unroll
+    for (int ks = 1; ks < 4; ++ks) s = mfma32(ka[ks], qB[ks], s);
+    u32x4 va[4];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) va[2 * db + mm] = ld16(stage + off.v_off(db, kb, mm));
+    if (masked) mask(kb, s);
+    u32x4 pB[2];
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[8 * mm + i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pB[mm][j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+      l = sum_bf16x8(pB[mm], l);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) oacc[db] = mfma32(va[2 * db + mm], pB[mm], oacc[db]);
+  }
+
+  // Normalise and store query (l % 32)'s row (if valid); lse in natural-log units.
+  __device__ __forceinline__ void finish(bf16* orow, float* lse_ptr, bool valid) {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const float l_tot = sum_halves(l);
+    const float inv = 1.f / l_tot;
+    if (!valid) return;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hh;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+    if (lse_ptr != nullptr && hh == 0) *lse_ptr = (m + __log2f(l_tot)) * 0.6931471805599453f;
   }
 };
 

@@ -99,6 +99,12 @@ void compact_shape(const sga::Geom& g, int s_h, int s_w, int* mk, int* has_mean,
 size_t elt_size(const sga_geom* g) { return g->dtype == SGA_BF16 ? 2 : 4; }
 
 // FlashLaunch of a dense_global_attn call (validated geometry and keys).
+sga_status check_fits(const sga::FlashLaunch& p) {
+  if (!sga::flash_bf16_fits(p))
+    return fail(SGA_ERR_UNSUPPORTED, "too many keys or heads for the bf16 kernel's 31-bit tile extents");
+  return SGA_OK;
+}
+
 sga::FlashLaunch dense_launch(const sga::Geom& g, int64_t n_keys, int32_t frame_local) {
   sga::FlashLaunch p{};
   p.g = g;
@@ -154,6 +160,7 @@ sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
   p.lse = lse;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (geom->dtype != SGA_BF16) return from_hip(sga::launch_flash_f32(p, s), "dense_global_attn launch");
+  if (sga_status st = check_fits(p)) return st;
   const size_t need = sga::flash_bf16_workspace(p);
   if (ws == nullptr || ws_bytes < need)
     return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
@@ -286,6 +293,7 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   if (mode == 1) {  // frame attention: the V^T staging is a prefix of the workspace
     p.mode = sga::FLASH_FRAME;
     if (!bf) return from_hip(sga::launch_flash_f32(p, s), "subsampled_global_attn (frame) launch");
+    if (sga_status st = check_fits(p)) return st;
     const size_t need = sga::flash_bf16_workspace(p);
     if (ws == nullptr || ws_bytes < need)
       return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
@@ -300,17 +308,20 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
   int mk, has_mean, n_drop;
   compact_shape(g, stride_h, stride_w, &mk, &has_mean, &n_drop);
+  p.mode = sga::FLASH_SUBSAMPLED;
+  p.mk = mk;
+  p.has_mean = has_mean;
+  if (bf) {
+    if (sga_status st = check_fits(p)) return st;
+  }
   size_t half, flash;
   subsampled_layout(geom, g, stride_h, stride_w, &half, &flash);
   unsigned char* c_k = static_cast<unsigned char*>(ws);
   unsigned char* c_v = c_k + half;
   if (hipError_t e = sga::launch_sga_compact(g, bf, stride_h, stride_w, k, v, c_k, c_v, s))
     return from_hip(e, "subsampled_global_attn (compact) launch");
-  p.mode = sga::FLASH_SUBSAMPLED;
   p.ck = c_k;
   p.cv = c_v;
-  p.mk = mk;
-  p.has_mean = has_mean;
   p.mean_bias2 = (mean_log_count && n_drop > 0) ? (float)std::log2((double)n_drop) : 0.f;
   return from_hip(bf ? sga::launch_flash_bf16(p, c_k + 2 * half, s) : sga::launch_flash_f32(p, s),
                   "subsampled_global_attn launch");

@@ -13,10 +13,19 @@
 // The per-tile math (attn_tile.hpp) keeps every per-query quantity inside the
 // lane that owns the query.
 //
+// Softmax: the scale log2(e)/sqrt(d) is folded into Q (rounded once to bf16),
+// and every query starts its accumulator at minus an upper bound of its logits,
+// |q'| max|k| (a small key-norm pass supplies max|k| per head), so the MFMA
+// returns logit - bound and a probability costs a single v_exp: no per-score
+// scaling, subtraction or running maximum, and no rescaling (attn_tile.hpp,
+// FlashWaveState). A workgroup whose rows' probabilities underflowed because
+// the bound was far above their true maximum flags itself, and a second launch
+// of the kernel redoes exactly those workgroups with the online softmax.
+//
 // Data movement: keys stream in tiles of 64 through a ring of LDS stages.
 // Every K row and every V^T row of a tile moves from HBM/L2 straight into LDS
-// with 16-byte direct loads (global_load_lds_dwordx4) issued one or two tiles
-// ahead -- no registers, no VALU address work per tile, no LDS write
+// with 16-byte direct buffer loads (buffer_load_dwordx4 ... lds) issued two
+// tiles ahead -- no registers, no VALU address work per tile, no LDS write
 // instructions. The swizzled LDS layouts are produced by choosing which
 // 16-byte chunk each lane fetches. V^T comes from a staging pass (vt_prepare)
 // that already holds V transposed in the MFMA operand's key order. A tile is
@@ -41,16 +50,21 @@ constexpr int kBlockM = kWaves * 32;         // 128 queries per workgroup
 constexpr int kRowsPerWave = 64 / kWaves;    // K rows and V^T rows each wave fetches per tile
 constexpr int kLoadsPerTile = 2 * kRowsPerWave / 8;  // 16-byte direct loads per lane per tile
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
-// Occupancy: the kernel is issue- and latency-bound, so it runs with more
-// resident waves and a shorter LDS ring rather than fewer waves with a deep
-// prefetch (measured on MI355X at 128 frames: 4 stages / 2 waves per SIMD
-// 35.3%, 3 / 3 38.1%, 2 / 4 39.0% of bf16 peak for dense attention; the
-// subsampled form, with more scalar bookkeeping, does best at 3 / 3).
-template <int MODE>
-struct Ring {
-  static constexpr int stages = (MODE == 2) ? 3 : 2;
-  static constexpr int wg_per_cu = (MODE == 2) ? 3 : 4;
-};
+// Key-norm partial maxima per head (the logit bound's max|k|).
+constexpr int kNormChunks = 256;
+// Margin on |q'| max|k| for the rounding of the norms, of the fp32 scores and
+// of the bf16 mean keys (the normalised result does not depend on it).
+constexpr float kBoundMargin = 1.0078125f;  // 1 + 2^-7
+// A row whose probabilities against the bound sum below this is redone exactly:
+// every key then within 2^-25 of the row's total weight is a normal float.
+constexpr float kLooseBoundSum = 8.271806125530277e-25f;  // 2^-80
+// Occupancy: 3 workgroups (12 waves) per CU with a 3-stage LDS ring (144 KiB).
+// At 4 workgroups per CU the 128-VGPR budget makes the compiler spill inside
+// the tile loop; measured on MI355X at 128 frames, dense attention runs at
+// 44.1% of bf16 peak with 3 stages / 3 workgroups, 43.1% with 2 / 3 and 37.4%
+// with 2 / 4 (spilling).
+constexpr int kStages = 3;
+constexpr int kWgPerCu = 3;
 
 enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
 
@@ -70,6 +84,9 @@ struct FlashArgs {
   int mk;            // SUBSAMPLED: kept rows per frame
   int has_mean;      // SUBSAMPLED: one mean row per frame follows the kept part
   float mean_bias2;  // SUBSAMPLED: log2(#dropped) added to mean rows' logits, or 0
+  float bound_extra; // added to every query's logit bound: mean_bias2 if mean rows exist
+  const float* knorm2;  // [H, kNormChunks] maxima of |k|^2
+  unsigned char* redo;  // [n_logical] 1: the workgroup's rows need the exact pass
   float scale_log2;  // log2(e) / sqrt(d)
   int n_qtiles;      // GLOBAL: tiles over T; else tiles per frame
   int n_logical;     // logical workgroups
@@ -86,8 +103,18 @@ struct Segment {
   long long n;
 };
 
-__device__ __forceinline__ void lds_dma16(const void* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// 16-byte direct load into LDS through a buffer resource: the base and the
+// extent are wave-uniform (SGPRs) and the lane's 32-bit offset is fixed for the
+// kernel; a lane whose 16 bytes reach past the extent gets zeros, no access.
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                          unsigned char* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, (int)voff, 0, 0, 0);
 }
 
 // Wait until at most N direct loads of this lane are in flight, then meet the
@@ -102,11 +129,13 @@ __device__ __forceinline__ void wait_and_meet() {
   asm volatile("" ::: "memory");
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_kernel(FlashArgs A) {
+// EXACT = false: the main pass against the logit bound; every workgroup records
+// in A.redo whether some row's probabilities underflowed. EXACT = true: only the
+// recorded workgroups run, redoing their rows with the exact online softmax.
+template <int MODE, bool EXACT>
+__global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int kStages = Ring<MODE>::stages;  // LDS ring
-  constexpr int kAhead = kStages - 1;          // tiles in flight ahead of the one consumed
+  constexpr int kAhead = kStages - 1;  // tiles in flight ahead of the one consumed
 
   int lid = blockIdx.x;
   if (A.remap) {
@@ -114,6 +143,7 @@ __global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_ke
     lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   }
   if (lid >= A.n_logical) return;
+  if (EXACT && A.redo[lid] == 0) return;
   int h, f = 0;
   long long q0, q_end;
   if (MODE == MODE_GLOBAL) {
@@ -153,9 +183,11 @@ __global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_ke
 
   // ---- direct tile loads -------------------------------------------------------
   // lane -> row r = wave * kRowsPerWave + 8 i + lane / 8 of the tile (a key row of
-  // K, a d row of V^T) and physical 16-byte chunk lane % 8. Every address is a
-  // per-tile scalar base plus a per-lane 32-bit offset fixed for the kernel, and
-  // the LDS destination is wave-uniform, so issuing a tile costs no VALU work.
+  // K, a d row of V^T) and physical 16-byte chunk lane % 8. Every load is a
+  // per-tile buffer resource (scalar) plus a per-lane 32-bit offset fixed for the
+  // kernel, and the LDS destination is wave-uniform, so issuing a tile costs no
+  // VALU work. A segment's last tile limits the K resource to its valid rows:
+  // the rows past the end load as zeros (and are masked).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int ld_r = lane >> 3, ld_p = lane & 7;
   uint32_t k_off[kRowsPerWave / 8], v_off0[kRowsPerWave / 8], v_off1[kRowsPerWave / 8];
@@ -172,24 +204,16 @@ __global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_ke
     const bool second = j >= nt0;
     const Segment& sg = second ? seg1 : seg0;
     const long long u0 = (second ? j - nt0 : j) * kTileKeys;
-    const char* kb = reinterpret_cast<const char*>(sg.k + (sg.k_row0 + u0) * rs + hoff);
-    const char* vb = reinterpret_cast<const char*>(sg.vt + hoff * sg.vt_ld + sg.vt_col0 + u0);
+    const long long rows = min((long long)kTileKeys, sg.n - u0);
+    const auto kr = buffer_rsrc(sg.k + (sg.k_row0 + u0) * rs + hoff, rows * rs * 2);
+    const auto vr = buffer_rsrc(sg.vt + hoff * sg.vt_ld + sg.vt_col0 + u0,
+                                kHeadDim * sg.vt_ld * 2);
     unsigned char* kdst = stage + wave_u * kRowsPerWave * 128;
     unsigned char* vdst = kdst + kTileKBytes;
-    if (u0 + kTileKeys <= sg.n) {
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave / 8; ++i) {
-        lds_dma16(kb + k_off[i], kdst + 8 * i * 128);
-        lds_dma16(vb + (second ? v_off1[i] : v_off0[i]), vdst + 8 * i * 128);
-      }
-    } else {  // last tile of a segment: rows past its end re-read its last row (masked)
-#pragma unroll
-      for (int i = 0; i < kRowsPerWave / 8; ++i) {
-        const long long r = wave_u * kRowsPerWave + 8 * i + ld_r;
-        const long long clamp = (u0 + r < sg.n) ? 0 : (sg.n - 1 - u0 - r) * rs * 2;
-        lds_dma16(kb + k_off[i] + clamp, kdst + 8 * i * 128);
-        lds_dma16(vb + (second ? v_off1[i] : v_off0[i]), vdst + 8 * i * 128);
-      }
+    for (int i = 0; i < kRowsPerWave / 8; ++i) {
+      lds_dma16(kr, k_off[i], kdst + 8 * i * 128);
+      lds_dma16(vr, second ? v_off1[i] : v_off0[i], vdst + 8 * i * 128);
     }
   };
 
@@ -200,91 +224,198 @@ __global__ __launch_bounds__(kThreads, Ring<MODE>::wg_per_cu) void flash_bf16_ke
     const long long a = (j - nt0) * kTileKeys, b = a + kTileKeys;
     return b > seg1.n || (a < own1 && b > own0) || (A.has_mean && b > mean0);
   };
-  auto apply_mask = [&](long long j, f32x16 s[2]) {
+  // (logits in log2 units: the mean rows' bias adds as it is). Every bound is
+  // taken relative to the half-tile's first key and clamped to [-1, 64], so the
+  // per-score tests are 32-bit compares against wave-uniform values.
+  auto apply_mask = [&](long long j, int kb, f32x16& s) {
     const bool second = j >= nt0;
-    const long long u0 = (second ? j - nt0 : j) * kTileKeys;
-    const long long n = second ? seg1.n : seg0.n;
-    const float bias = A.mean_bias2 / c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const long long u = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        bool ok = u < n;
-        float add = 0.f;
-        if (MODE == MODE_SUBSAMPLED && second) {
-          ok = ok && !(u >= own0 && u < own1) && !(A.has_mean && u == mean0 + f);
-          if (A.has_mean && u >= mean0) add = bias;
-        }
-        s[kb][i] = ok ? s[kb][i] + add : -INFINITY;
+    const long long u0 = (second ? j - nt0 : j) * kTileKeys + kb * 32;
+    auto rel = [&](long long x) { return (int)max(-1LL, min(x - u0, 64LL)); };
+    const int lim = rel(second ? seg1.n : seg0.n);
+    int own_a = 64, own_b = 64, own_mean = -1, mean_a = 64;
+    if (MODE == MODE_SUBSAMPLED && second) {
+      own_a = rel(own0);
+      own_b = rel(own1);
+      if (A.has_mean) {
+        own_mean = rel(mean0 + f);
+        mean_a = rel(mean0);
       }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = 8 * (i >> 2) + 4 * hh + (i & 3);
+      const bool ok = u < lim && !(u >= own_a && u < own_b) && u != own_mean;
+      s[i] = ok ? s[i] + (u >= mean_a ? A.mean_bias2 : 0.f) : -INFINITY;
+    }
   };
 
   const long long qrow = q0 + wave * 32 + li;
   const bool qvalid = qrow < q_end;
   u32x4 qB[4];
-  load_q_operand(A.q + (qvalid ? qrow : q0) * rs + hoff, qvalid, qB);
+  load_q_operand_scaled(A.q + (qvalid ? qrow : q0) * rs + hoff, qvalid, c, qB);
 
-  WaveAttnState st;
-  st.init();
   TileLaneOffsets off;
   off.init();
 
+  // The tile loop: a ring of kStages LDS stages, kAhead tiles in flight;
+  // step(j, stage, masked) consumes tile j.
+  auto run_tiles = [&](auto&& step) {
 #pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (j < n_tiles) issue_tile(j, smem + j * kStageBytes);
-  static_assert(kStages >= 2 && kStages <= 4, "ring of 2 to 4 stages");
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  auto body = [&](long long j, auto cur_c) {
-    constexpr int cur = decltype(cur_c)::value;
-    constexpr int refill = (cur + kAhead) % kStages;
-    const long long left = n_tiles - 1 - j;  // tiles after j already in flight: min(kAhead-1, left)
-    if (left >= kAhead - 1) {
-      wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
-    } else if (kAhead > 2 && left == 1) {
-      wait_and_meet<kLoadsPerTile>();
-    } else {
-      wait_and_meet<0>();
+    for (int j = 0; j < kAhead; ++j)
+      if (j < n_tiles) issue_tile(j, smem + j * kStageBytes);
+    static_assert(kStages >= 2 && kStages <= 4, "ring of 2 to 4 stages");
+    auto body = [&](long long j, auto cur_c) {
+      constexpr int cur = decltype(cur_c)::value;
+      constexpr int refill = (cur + kAhead) % kStages;
+      const long long left = n_tiles - 1 - j;  // tiles after j in flight: min(kAhead-1, left)
+      if (left >= kAhead - 1) {
+        wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
+      } else if (kAhead > 2 && left == 1) {
+        wait_and_meet<kLoadsPerTile>();
+      } else {
+        wait_and_meet<0>();
+      }
+      if (j + kAhead < n_tiles) issue_tile(j + kAhead, smem + refill * kStageBytes);
+      step(j, smem + cur * kStageBytes, needs_mask(j));
+    };
+    for (long long j = 0; j < n_tiles; j += kStages) {
+      body(j, std::integral_constant<int, 0>{});
+      if (j + 1 < n_tiles) body(j + 1, std::integral_constant<int, 1>{});
+      if constexpr (kStages > 2) {
+        if (j + 2 < n_tiles) body(j + 2, std::integral_constant<int, 2>{});
+      }
+      if constexpr (kStages > 3) {
+        if (j + 3 < n_tiles) body(j + 3, std::integral_constant<int, 3>{});
+      }
     }
-    if (j + kAhead < n_tiles) issue_tile(j + kAhead, smem + refill * kStageBytes);
-    const unsigned char* stage = smem + cur * kStageBytes;
-    f32x16 s[2];
-    st.scores(stage, off, qB, s);
-    if (needs_mask(j)) apply_mask(j, s);
-    st.consume(s, stage, off, c, false, true);
   };
-  for (long long j = 0; j < n_tiles; j += kStages) {
-    body(j, I0{});
-    if (j + 1 < n_tiles) body(j + 1, I1{});
-    if constexpr (kStages > 2) {
-      if (j + 2 < n_tiles) body(j + 2, std::integral_constant<int, 2>{});
+
+  bf16* orow = A.o + qrow * rs + hoff;
+  float* lse_ptr = A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr;
+  if constexpr (EXACT) {
+    // scores already in log2 units, so c = 1
+    WaveAttnState ex;
+    ex.init();
+    run_tiles([&](long long j, const unsigned char* stage, bool masked) {
+      f32x16 sc[2];
+      ex.scores(stage, off, qB, sc);
+      if (masked) {
+        apply_mask(j, 0, sc[0]);
+        apply_mask(j, 1, sc[1]);
+      }
+      ex.consume(sc, stage, off, 1.f, false, true);
+    });
+    ex.finish(orow, lse_ptr, qvalid, 1.f);
+  } else {
+    // Upper bound of the query's logits (log2 units): |q'| max|k| with a margin
+    // for the rounding of |q'|, of max|k| and of the bf16 mean keys, plus the
+    // mean rows' bias. The key-norm partials are per (head, chunk) maxima of |k|^2.
+    float bound;
+    {
+      float q2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float a0 = lo_bf16(qB[ks][jj]), a1 = hi_bf16(qB[ks][jj]);
+          q2 = fmaf(a0, a0, fmaf(a1, a1, q2));
+        }
+      q2 = sum_halves(q2);
+      float k2 = 0.f;
+      for (int i = lane; i < kNormChunks; i += 64) k2 = fmaxf(k2, A.knorm2[h * kNormChunks + i]);
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, sh));
+      bound = sqrtf(q2) * sqrtf(k2) * kBoundMargin + A.bound_extra;
     }
-    if constexpr (kStages > 3) {
-      if (j + 3 < n_tiles) body(j + 3, std::integral_constant<int, 3>{});
-    }
+    FlashWaveState st;
+    st.init(bound);
+    run_tiles([&](long long j, const unsigned char* stage, bool masked) {
+      auto mask = [&](int kb, f32x16& s) { apply_mask(j, kb, s); };
+      st.half(stage, off, 0, qB, masked, mask);
+      st.half(stage, off, 1, qB, masked, mask);
+    });
+    // A bound far above a row's true maximum leaves its probabilities below
+    // the fp32 range: the workgroup is then redone by the exact pass.
+    const bool loose = !(sum_halves(st.l) >= kLooseBoundSum);
+    const int any_loose = __syncthreads_or(loose);
+    if (tid == 0) A.redo[lid] = any_loose ? 1 : 0;
+    st.finish(orow, lse_ptr, qvalid);
   }
-  st.finish(A.o + qrow * rs + hoff, A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr, qvalid, c);
+}
+
+// Per (head, chunk) maximum of |k|^2 over the rows of K: a workgroup per
+// (head, chunk), 8 lanes per 128-byte key row.
+__global__ __launch_bounds__(256) void knorm_partial_kernel(const bf16* __restrict__ k,
+                                                            long long n_rows, int n_heads,
+                                                            float* __restrict__ out) {
+  const int h = blockIdx.x / kNormChunks, chunk = blockIdx.x % kNormChunks;
+  const long long per = (n_rows + kNormChunks - 1) / kNormChunks;
+  const long long r0 = chunk * per, r1 = min(r0 + per, n_rows);
+  const long long rs = (long long)n_heads * kHeadDim;
+  const int t = threadIdx.x, part = t & 7;
+  float best = 0.f;
+  for (long long r = r0 + (t >> 3); r < r1; r += 32) {
+    const u32x4 w = ld16(k + r * rs + (long long)h * kHeadDim + part * 8);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = lo_bf16(w[j]), a1 = hi_bf16(w[j]);
+      acc = fmaf(a0, a0, fmaf(a1, a1, acc));
+    }
+#pragma unroll
+    for (int sh = 1; sh < 8; sh <<= 1) acc += __shfl_xor(acc, sh);
+    best = fmaxf(best, acc);
+  }
+#pragma unroll
+  for (int sh = 8; sh < 64; sh <<= 1) best = fmaxf(best, __shfl_xor(best, sh));
+  __shared__ float wmax[4];
+  if ((t & 63) == 0) wmax[t >> 6] = best;
+  __syncthreads();
+  if (t == 0) out[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 }  // namespace
 
+// Workspace: the V^T staging (a multiple of 8 KiB), then the key-norm partials.
+// V^T row length (columns) of the staging of K/V (and of the compacted set).
+static long long vt_ld_main(const FlashLaunch& p) {
+  if (p.mode == FLASH_GLOBAL) return (p.n_keys + 63) / 64 * 64;
+  return (long long)((p.g.L + 63) / 64 * 64) * p.g.n_frames;
+}
+static long long vt_ld_compact(const FlashLaunch& p) {
+  if (p.mode != FLASH_SUBSAMPLED) return 0;
+  return ((long long)p.g.n_frames * (p.mk + p.has_mean) + 63) / 64 * 64;
+}
+static long long logical_workgroups(const FlashLaunch& p) {
+  if (p.mode == FLASH_GLOBAL) return (p.g.T + kBlockM - 1) / kBlockM * p.g.n_heads;
+  return (long long)((p.g.L + kBlockM - 1) / kBlockM) * p.g.n_frames * p.g.n_heads;
+}
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace: the V^T staging (a multiple of 8 KiB), the key-norm partials,
+// the per-workgroup redo flags.
+static size_t vt_bytes(const FlashLaunch& p) {
+  return (size_t)p.g.n_heads * kHeadDim * (vt_ld_main(p) + vt_ld_compact(p)) * 2;
+}
+static size_t norm_bytes(const FlashLaunch& p) {
+  return round256((size_t)p.g.n_heads * kNormChunks * sizeof(float));
+}
+
 size_t flash_bf16_workspace(const FlashLaunch& p) {
-  if (p.mode == FLASH_GLOBAL) {
-    const long long ld = (p.n_keys + 63) / 64 * 64;
-    return (size_t)p.g.n_heads * kHeadDim * ld * 2;
-  }
-  const long long pitch = (p.g.L + 63) / 64 * 64;
-  size_t bytes = (size_t)p.g.n_heads * kHeadDim * pitch * p.g.n_frames * 2;
-  if (p.mode == FLASH_SUBSAMPLED) {
-    const long long rows = (long long)p.g.n_frames * (p.mk + p.has_mean);
-    bytes += (size_t)p.g.n_heads * kHeadDim * ((rows + 63) / 64 * 64) * 2;
-  }
-  return bytes;
+  return vt_bytes(p) + norm_bytes(p) + round256((size_t)logical_workgroups(p));
+}
+
+bool flash_bf16_fits(const FlashLaunch& p) {
+  // buffer extents of one tile: 64 K rows, 64 V^T rows, in 31 bits
+  const long long lim = 0x7fffffffLL;
+  return (long long)kTileKeys * p.g.n_heads * kHeadDim * 2 <= lim &&
+         (long long)kHeadDim * vt_ld_main(p) * 2 <= lim &&
+         (long long)kHeadDim * vt_ld_compact(p) * 2 <= lim &&
+         logical_workgroups(p) <= 0x7ffffff0LL;
 }
 
 hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream) {
+  if (!flash_bf16_fits(p)) return hipErrorInvalidValue;
   FlashArgs A{};
   A.q = static_cast<const bf16*>(p.q);
   A.o = static_cast<bf16*>(p.o);
@@ -297,49 +428,60 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   A.has_mean = p.has_mean;
   A.mean_bias2 = p.mean_bias2;
   A.scale_log2 = kLog2e / sqrtf((float)kHeadDim);
-  bf16* vt = static_cast<bf16*>(ws);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  bf16* vt = reinterpret_cast<bf16*>(wsb);
+  float* knorm2 = reinterpret_cast<float*>(wsb + vt_bytes(p));
+  A.redo = wsb + vt_bytes(p) + norm_bytes(p);
+  A.vt = vt;
+  A.vt_ld = vt_ld_main(p);
   hipError_t e;
-  long long n_logical;
   if (p.mode == FLASH_GLOBAL) {
-    A.vt_ld = (p.n_keys + 63) / 64 * 64;
     e = launch_vt_prepare(p.v, p.g.n_heads, p.n_keys, p.n_keys, A.vt_ld, A.vt_ld, vt, stream);
     if (e != hipSuccess) return e;
     A.n_qtiles = (int)((p.g.T + kBlockM - 1) / kBlockM);
-    n_logical = (long long)A.n_qtiles * p.g.n_heads;
     A.remap = 0;
   } else {
     A.vt_pitch = (p.g.L + 63) / 64 * 64;
-    A.vt_ld = (long long)A.vt_pitch * p.g.n_frames;
     e = launch_vt_prepare(p.v, p.g.n_heads, p.g.T, p.g.L, A.vt_pitch, A.vt_ld, vt, stream);
     if (e != hipSuccess) return e;
     if (p.mode == FLASH_SUBSAMPLED) {
       const long long rows = (long long)p.g.n_frames * (p.mk + p.has_mean);
-      A.cvt_ld = (rows + 63) / 64 * 64;
+      A.cvt_ld = vt_ld_compact(p);
       bf16* cvt = vt + (size_t)p.g.n_heads * kHeadDim * A.vt_ld;
       e = launch_vt_prepare(p.cv, p.g.n_heads, rows, rows, A.cvt_ld, A.cvt_ld, cvt, stream);
       if (e != hipSuccess) return e;
       A.cvt = cvt;
     }
     A.n_qtiles = (p.g.L + kBlockM - 1) / kBlockM;
-    n_logical = (long long)A.n_qtiles * p.g.n_frames * p.g.n_heads;
     A.remap = 1;
   }
-  A.vt = vt;
-  if (n_logical > 0x7ffffff0LL) return hipErrorInvalidValue;
-  A.n_logical = (int)n_logical;
+  // key-norm partials over every key the queries can meet (the compacted
+  // rows are copies and means of these, covered by the bound's margin)
+  const long long norm_rows = p.mode == FLASH_GLOBAL ? p.n_keys : p.g.T;
+  hipLaunchKernelGGL(knorm_partial_kernel, dim3(p.g.n_heads * kNormChunks), dim3(256), 0, stream,
+                     static_cast<const bf16*>(p.k), norm_rows, p.g.n_heads, knorm2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  A.knorm2 = knorm2;
+  A.bound_extra = (p.mode == FLASH_SUBSAMPLED && p.has_mean) ? p.mean_bias2 : 0.f;
+  A.n_logical = (int)logical_workgroups(p);
   const int grid = A.remap ? ((A.n_logical + 7) / 8) * 8 : A.n_logical;
+  // the main pass, then the exact pass over the workgroups it flagged
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kStages * kStageBytes, stream, A);
+  };
   switch (p.mode) {
     case FLASH_GLOBAL:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_GLOBAL>, dim3(grid), dim3(kThreads),
-                         Ring<MODE_GLOBAL>::stages * kStageBytes, stream, A);
+      launch(flash_bf16_kernel<MODE_GLOBAL, false>);
+      launch(flash_bf16_kernel<MODE_GLOBAL, true>);
       break;
     case FLASH_FRAME:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_FRAME>, dim3(grid), dim3(kThreads),
-                         Ring<MODE_FRAME>::stages * kStageBytes, stream, A);
+      launch(flash_bf16_kernel<MODE_FRAME, false>);
+      launch(flash_bf16_kernel<MODE_FRAME, true>);
       break;
     default:
-      hipLaunchKernelGGL(flash_bf16_kernel<MODE_SUBSAMPLED>, dim3(grid), dim3(kThreads),
-                         Ring<MODE_SUBSAMPLED>::stages * kStageBytes, stream, A);
+      launch(flash_bf16_kernel<MODE_SUBSAMPLED, false>);
+      launch(flash_bf16_kernel<MODE_SUBSAMPLED, true>);
       break;
   }
   return hipGetLastError();

@@ -30,9 +30,11 @@ struct FlashLaunch {
 };
 
 // bf16 MFMA flash attention (flash_bf16.hip). ws holds the V^T staging of the
-// values (and of the compacted values in SUBSAMPLED mode); its size is
-// flash_bf16_workspace(p).
+// values (and of the compacted values in SUBSAMPLED mode), the key-norm
+// partials and the redo flags; its size is flash_bf16_workspace(p).
+// flash_bf16_fits(p) is false for sizes past the kernel's 31-bit tile extents.
 size_t flash_bf16_workspace(const FlashLaunch& p);
+bool flash_bf16_fits(const FlashLaunch& p);
 hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream);
 // V^T staging (vt_prepare.hip): vt[(h*64 + d)*ld + col] = v[key(col), h, d], keys
 // in segments of seg_len padded to seg_pad columns, MFMA key order in 16-column groups.

@@ -122,16 +122,22 @@ def r256(x):
 def test_workspace_sizes():
     g = geom(n_frames=256)
     T = 256 * 1374
-    # dense bf16: V^T staging, keys rounded up to 64 columns, 16 heads x 64 rows of d
-    assert _ws(g, 2, 0, 0) == (OK, 16 * 64 * ((T + 63) // 64 * 64) * 2)
-    assert _ws(g, 2, 25600, 0) == (OK, 16 * 64 * 25600 * 2)
-    # frame mode: every frame padded to 1408 columns
-    assert _ws(g, 2, 0, 1) == (OK, 16 * 64 * 1408 * 256 * 2)
+    # dense bf16: V^T staging, keys rounded up to 64 columns, 16 heads x 64 rows
+    # of d, then 256 key-norm partial maxima per head (fp32), then one redo flag
+    # byte per workgroup of 128 queries
+    norms = 16 * 256 * 4
+    flags = r256(-(-T // 128) * 16)
+    assert _ws(g, 2, 0, 0) == (OK, 16 * 64 * ((T + 63) // 64 * 64) * 2 + norms + flags)
+    assert _ws(g, 2, 25600, 0) == (OK, 16 * 64 * 25600 * 2 + norms + flags)
+    # frame mode: every frame padded to 1408 columns, 11 workgroups per frame
+    frame_flags = r256(11 * 256 * 16)
+    assert _ws(g, 2, 0, 1) == (OK, 16 * 64 * 1408 * 256 * 2 + norms + frame_flags)
     assert _ws(g, 2, 5, 1)[0] == INVALID
     # subsampled: per frame 5 specials + 100 kept + 1 mean = 106 rows of K and V,
     # then the frame-padded V^T and the V^T of the 27,136 compacted rows
     half = r256(256 * 106 * 16 * 64 * 2)
-    flash = r256(16 * 64 * 1408 * 256 * 2 + 16 * 64 * ((256 * 106 + 63) // 64 * 64) * 2)
+    flash = r256(16 * 64 * 1408 * 256 * 2 + 16 * 64 * ((256 * 106 + 63) // 64 * 64) * 2 + norms
+                 + frame_flags)
     assert _ws(g, 1, 4, 4) == (OK, 2 * half + flash)
     assert sga.compact_rows(g, 4, 4) == (105, 1)
     # fp32 keeps only the compacted set, dense needs nothing

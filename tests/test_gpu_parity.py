@@ -158,6 +158,31 @@ def test_small_every_op(geom, top_k, stride):
     assert_close(host(o_sf), oracle.frame_attention(qh, kh, vh, geom), dt, "subsampled frame mode")
 
 
+def test_loose_bound_redo():
+    """Rows whose logits sit far below |q| max|k|: the bf16 kernels start each
+    query at that bound, so here every probability of the first pass underflows
+    and the workgroups holding these rows must redo them exactly."""
+    geom = Geometry(3, 5, 13, 11, 2, 64, "bf16")
+    _announce(f"loose logit bound {geom}")
+    q, k, v = make_qkv(geom, seed=21, device=DEV, distribution="scene")
+    far = [0, 1, 2, 15, 130, 300, 301, 443]
+    k[7] = 0
+    k[7, :, 0] = 40.0   # one key of norm 40 along d = 0 ...
+    q[far] = 0
+    q[far, :, 1] = 40.0  # ... queries of norm 40 orthogonal to it: bound 288 log2 units
+    qh, kh, vh = host(q), host(k), host(v)
+    o, lse = sga.dense_global_attn(q, k, v, geom, want_lse=True)
+    of = sga.dense_global_attn(q, k, v, geom, frame_local=True)
+    os_ = sga.subsampled_global_attn(q, k, v, geom, 2, 2)
+    _sync()
+    ro, rlse = oracle.dense_attention(qh, kh, vh, with_lse=True)
+    assert_close(host(o), ro, "bf16", "dense (loose bound)")
+    assert_close(host(lse), rlse, "bf16", "dense lse (loose bound)")
+    assert_close(host(of), oracle.frame_attention(qh, kh, vh, geom), "bf16", "frame (loose bound)")
+    assert_close(host(os_), oracle.subsampled_attention(qh, kh, vh, geom, 2, 2), "bf16",
+                 "subsampled (loose bound)")
+
+
 def test_invariants_on_gpu():
     """The pages' reductions hold on the GPU path too: K = all blocks with the
     gate forced to the fine branch is dense; stride 1x1 is dense."""
