@@ -14,6 +14,7 @@ Prints one JSON line. `value` = tokens of the batch / seconds per step.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -159,6 +160,10 @@ def main():
                 "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "flop_per_launch": flop_dense, "traffic": None}
+    traffic = measured_traffic(args.workload)
+    if traffic is not None:
+        roofline["traffic"] = traffic
+        roofline["traffic_unit"] = "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE scaled)"
 
     cpu = None
     if args.cpu_rows > 0:
@@ -178,6 +183,25 @@ def main():
         "layers": layers, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "flash_dense_scene1000_traffic.json")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dense kernel from the committed counter
+    record, only while the kernel sources are the ones it was taken from."""
+    if workload != "scene1000" or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    with open(TRAFFIC_RECORD) as fh:
+        rec = json.load(fh)
+    digest = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as fh:
+            digest.update(fh.read())
+    if digest.hexdigest() != rec["sources_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def cpu_baseline(q, k, v, w, b, geom, wl, n_rows, seed):

@@ -269,37 +269,48 @@ struct FlashWaveState {
     l = 0.f;
   }
 
-  // Half kb (keys 32 kb .. 32 kb + 31) of a staged tile. mask(kb, s) applies the
-  // tile's key mask and logit bias (log2 units) when `masked`.
-  template <class MaskFn>
-  __device__ __forceinline__ void half(const unsigned char* stage, const TileLaneOffsets& off,
-                                       int kb, const u32x4 qB[4], bool masked, MaskFn&& mask) {
-    u32x4 ka[4];
+  // One staged 64-key tile, straight-line: both halves' scores, then for each
+  // half its probabilities and O^T += V^T P^T. With MASKED, mask(kb, s) applies
+  // the tile's key mask and logit bias (log2 units) to half kb's scores.
+  template <bool MASKED, class MaskFn>
+  __device__ __forceinline__ void tile(const unsigned char* stage, const TileLaneOffsets& off,
+                                       const u32x4 qB[4], MaskFn&& mask) {
+    f32x16 s[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ka[ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
-    f32x16 s = mfma32(ka[0], qB[0], negm);
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 ka[4];
 #pragma unroll
-    for (int ks = 1; ks < 4; ++ks) s = mfma32(ka[ks], qB[ks], s);
-    u32x4 va[4];
+      for (int ks = 0; ks < 4; ++ks) ka[ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
+      s[kb] = mfma32(ka[0], qB[0], negm);
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) va[2 * db + mm] = ld16(stage + off.v_off(db, kb, mm));
-    if (masked) mask(kb, s);
-    u32x4 pB[2];
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      float p[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[8 * mm + i]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pB[mm][j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
-      l = sum_bf16x8(pB[mm], l);
+      for (int ks = 1; ks < 4; ++ks) s[kb] = mfma32(ka[ks], qB[ks], s[kb]);
+    }
+    if constexpr (MASKED) {
+      mask(0, s[0]);
+      mask(1, s[1]);
     }
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 va[4];
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) oacc[db] = mfma32(va[2 * db + mm], pB[mm], oacc[db]);
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) va[2 * db + mm] = ld16(stage + off.v_off(db, kb, mm));
+      u32x4 pB[2];
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(s[kb][8 * mm + i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pB[mm][j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        l = sum_bf16x8(pB[mm], l);
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) oacc[db] = mfma32(va[2 * db + mm], pB[mm], oacc[db]);
+    }
   }
 
   // Normalise and store query (l % 32)'s row (if valid); lse in natural-log units.

@@ -59,10 +59,14 @@ constexpr float kBoundMargin = 1.0078125f;  // 1 + 2^-7
 // every key then within 2^-25 of the row's total weight is a normal float.
 constexpr float kLooseBoundSum = 8.271806125530277e-25f;  // 2^-80
 // Occupancy: 3 workgroups (12 waves) per CU with a 3-stage LDS ring (144 KiB).
-// At 4 workgroups per CU the 128-VGPR budget makes the compiler spill inside
-// the tile loop; measured on MI355X at 128 frames, dense attention runs at
-// 44.1% of bf16 peak with 3 stages / 3 workgroups, 43.1% with 2 / 3 and 37.4%
-// with 2 / 4 (spilling).
+// Measured on MI355X at 128 frames (dense attention, % of bf16 peak): 3 stages
+// and 3 workgroups 44-46%; 2 / 3 43%; 2 / 4, where the 128-VGPR budget makes the
+// compiler spill inside the tile loop, 37%; 8-wave workgroups sharing each tile
+// (2 waves per SIMD) 44%. A ping-pong schedule of two barrier-locked wave groups
+// per SIMD (one group on MFMA while the other computes probabilities) reached
+// only 30-39%: the per-phase barriers, LDS waits and scalar work cost more than
+// the forced overlap gains, where three free-running waves per SIMD overlap
+// MFMA and VALU work by themselves.
 constexpr int kStages = 3;
 constexpr int kWgPerCu = 3;
 
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
   for (int i = 0; i < kRowsPerWave / 8; ++i) {
     const int r = wave_u * kRowsPerWave + 8 * i + ld_r;
     const int kc = ld_p ^ ld_r;                               // K swizzle: chunk ^ (r & 7)
-    const int vc = ld_p ^ ld_r ^ ((2 * wave_u + i) & 7);      // V^T swizzle: chunk ^ swz(r)
+    const int vc = ld_p ^ ld_r ^ ((wave_u * (kRowsPerWave / 8) + i) & 7);  // V^T: chunk ^ swz(r)
     k_off[i] = (uint32_t)((r * rs + kc * 8) * 2);
     v_off0[i] = (uint32_t)((r * seg0.vt_ld + vc * 8) * 2);
     v_off1[i] = (uint32_t)((r * seg1.vt_ld + vc * 8) * 2);
@@ -217,12 +221,36 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
     }
   };
 
-  // logit mask/bias of tile j (boundary tiles only), applied in registers
-  auto needs_mask = [&](long long j) -> bool {
-    if (j < nt0) return (j + 1) * kTileKeys > seg0.n;
-    if (MODE != MODE_SUBSAMPLED) return false;
-    const long long a = (j - nt0) * kTileKeys, b = a + kTileKeys;
-    return b > seg1.n || (a < own1 && b > own0) || (A.has_mean && b > mean0);
+  // ---- tile order: every clean tile first, the masked ones after -------------
+  // Tile t (t < nt0: segment 0, else segment 1 tile t - nt0) needs a logit mask
+  // or bias when it holds a segment's end, the query frame's own compacted rows
+  // or mean rows. Those few tiles run after the clean ones, in a loop of their
+  // own, so that the masking code never occupies registers of the main loop.
+  // The order does not matter to the softmax sum.
+  //   clean:  segment 0 [0, c0), segment 1 [0, a1) and [b1, m1)
+  //   masked: segment 0 [c0, nt0), segment 1 [a1, min(b1, m1)) and [m1, nt1)
+  const long long nt1 = n_tiles - nt0;
+  const long long c0 = seg0.n / kTileKeys;
+  long long a1 = 0, b1 = 0, m1 = 0;
+  if (MODE == MODE_SUBSAMPLED) {
+    const long long clean_end = A.has_mean ? min(mean0, seg1.n) : seg1.n;
+    m1 = clean_end / kTileKeys;
+    a1 = min(own0 / kTileKeys, m1);
+    b1 = (own1 + kTileKeys - 1) / kTileKeys;
+  }
+  const long long n_clean = c0 + a1 + max(0LL, m1 - b1);
+  auto tile_of = [&](long long j) -> long long {
+    if (j < c0) return j;
+    j -= c0;
+    if (j < a1) return nt0 + j;
+    j -= a1;
+    if (j < m1 - b1) return nt0 + b1 + j;
+    j -= max(0LL, m1 - b1);
+    if (j < nt0 - c0) return c0 + j;
+    j -= nt0 - c0;
+    const long long own_masked = min(b1, m1) - a1;
+    if (j < own_masked) return nt0 + a1 + j;
+    return nt0 + m1 + (j - own_masked);
   };
   // (logits in log2 units: the mean rows' bias adds as it is). Every bound is
   // taken relative to the half-tile's first key and clamped to [-1, 64], so the
@@ -241,9 +269,14 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
         mean_a = rel(mean0);
       }
     }
+    // the lane's key base is made opaque here so that the 16 key offsets are
+    // formed inside the (rare) masked tile instead of being hoisted out of the
+    // tile loop into 16 live registers
+    int ubase = 4 * hh;
+    asm volatile("" : "+v"(ubase));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int u = 8 * (i >> 2) + 4 * hh + (i & 3);
+      const int u = 8 * (i >> 2) + ubase + (i & 3);
       const bool ok = u < lim && !(u >= own_a && u < own_b) && u != own_mean;
       s[i] = ok ? s[i] + (u >= mean_a ? A.mean_bias2 : 0.f) : -INFINITY;
     }
@@ -257,54 +290,56 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
   TileLaneOffsets off;
   off.init();
 
-  // The tile loop: a ring of kStages LDS stages, kAhead tiles in flight;
-  // step(j, stage, masked) consumes tile j.
-  auto run_tiles = [&](auto&& step) {
+  // The tile loop: a ring of kStages LDS stages, kAhead tiles in flight, in
+  // the order tile_of(0), tile_of(1), ...
+  static_assert(kStages == 3, "the main loop is written for a 3-stage ring");
 #pragma unroll
-    for (int j = 0; j < kAhead; ++j)
-      if (j < n_tiles) issue_tile(j, smem + j * kStageBytes);
-    static_assert(kStages >= 2 && kStages <= 4, "ring of 2 to 4 stages");
-    auto body = [&](long long j, auto cur_c) {
-      constexpr int cur = decltype(cur_c)::value;
-      constexpr int refill = (cur + kAhead) % kStages;
-      const long long left = n_tiles - 1 - j;  // tiles after j in flight: min(kAhead-1, left)
-      if (left >= kAhead - 1) {
-        wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
-      } else if (kAhead > 2 && left == 1) {
-        wait_and_meet<kLoadsPerTile>();
-      } else {
-        wait_and_meet<0>();
-      }
-      if (j + kAhead < n_tiles) issue_tile(j + kAhead, smem + refill * kStageBytes);
-      step(j, smem + cur * kStageBytes, needs_mask(j));
-    };
-    for (long long j = 0; j < n_tiles; j += kStages) {
-      body(j, std::integral_constant<int, 0>{});
-      if (j + 1 < n_tiles) body(j + 1, std::integral_constant<int, 1>{});
-      if constexpr (kStages > 2) {
-        if (j + 2 < n_tiles) body(j + 2, std::integral_constant<int, 2>{});
-      }
-      if constexpr (kStages > 3) {
-        if (j + 3 < n_tiles) body(j + 3, std::integral_constant<int, 3>{});
-      }
+  for (int j = 0; j < kAhead; ++j)
+    if (j < n_tiles) issue_tile(tile_of(j), smem + j * kStageBytes);
+  // wait for tile j (the tiles after it in flight: min(kAhead - 1, left)), meet
+  // the other waves (all done with tile j - 1's stage), refill that stage
+  auto enter = [&](long long j, unsigned char* refill_stage) {
+    const long long left = n_tiles - 1 - j;
+    if (left >= kAhead - 1) {
+      wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
+    } else {
+      wait_and_meet<0>();
+    }
+    if (j + kAhead < n_tiles) issue_tile(tile_of(j + kAhead), refill_stage);
+  };
+  // the clean tiles in whole rounds of the ring; the rest (a partial round and
+  // the masked tiles) one by one with runtime stage addresses
+  const long long n_main = n_clean / kStages * kStages;
+  auto run_rest = [&](auto&& step) {
+    for (long long j = n_main; j < n_tiles; ++j) {
+      const int cur = (int)(j % kStages);
+      enter(j, smem + ((cur + kAhead) % kStages) * kStageBytes);
+      step(tile_of(j), smem + cur * kStageBytes);
     }
   };
-
   bf16* orow = A.o + qrow * rs + hoff;
   float* lse_ptr = A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr;
   if constexpr (EXACT) {
     // scores already in log2 units, so c = 1
     WaveAttnState ex;
     ex.init();
-    run_tiles([&](long long j, const unsigned char* stage, bool masked) {
+    auto step = [&](long long t, const unsigned char* stage, bool masked) {
       f32x16 sc[2];
       ex.scores(stage, off, qB, sc);
       if (masked) {
-        apply_mask(j, 0, sc[0]);
-        apply_mask(j, 1, sc[1]);
+        apply_mask(t, 0, sc[0]);
+        apply_mask(t, 1, sc[1]);
       }
       ex.consume(sc, stage, off, 1.f, false, true);
-    });
+    };
+    for (long long j = 0; j < n_main; j += kStages) {
+#pragma unroll
+      for (int cur = 0; cur < kStages; ++cur) {
+        enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+        step(tile_of(j + cur), smem + cur * kStageBytes, false);
+      }
+    }
+    run_rest([&](long long t, const unsigned char* stage) { step(t, stage, true); });
     ex.finish(orow, lse_ptr, qvalid, 1.f);
   } else {
     // Upper bound of the query's logits (log2 units): |q'| max|k| with a margin
@@ -329,10 +364,15 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
     }
     FlashWaveState st;
     st.init(bound);
-    run_tiles([&](long long j, const unsigned char* stage, bool masked) {
-      auto mask = [&](int kb, f32x16& s) { apply_mask(j, kb, s); };
-      st.half(stage, off, 0, qB, masked, mask);
-      st.half(stage, off, 1, qB, masked, mask);
+    for (long long j = 0; j < n_main; j += kStages) {
+#pragma unroll
+      for (int cur = 0; cur < kStages; ++cur) {
+        enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+        st.tile<false>(smem + cur * kStageBytes, off, qB, [](int, f32x16&) {});
+      }
+    }
+    run_rest([&](long long t, const unsigned char* stage) {
+      st.tile<true>(stage, off, qB, [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
     });
     // A bound far above a row's true maximum leaves its probabilities below
     // the fp32 range: the workgroup is then redone by the exact pass.
