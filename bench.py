@@ -84,6 +84,8 @@ def main():
     names = ["dense", "frame", "gsa_pool", "gsa_compressed", "gsa_topk", "gsa_fine", "gsa_gate",
              "sga"]
 
+    last = {}
+
     def step(ev):
         i = 0
         ev[i].record(); i += 1
@@ -96,6 +98,7 @@ def main():
         o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
         ev[i].record(); i += 1
         idx = sga.gsa_select_topk(q32, k32, geom, wl.top_k)
+        last["idx"] = idx
         ev[i].record(); i += 1
         o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, wl.top_k)
         ev[i].record(); i += 1
@@ -138,6 +141,7 @@ def main():
     keys_sga = geom.tokens_per_frame + (N - 1) * (mk + has_mean)
     flop_sga = 4.0 * T * keys_sga * d * H
     t_gsa = sum(per[n] for n in names if n.startswith("gsa_"))
+    gsa_roof = gsa_rooflines(geom, wl, per, last["idx"])
     layers = {
         "dense": {"ms": per["dense"], "tokens_per_s": T / per["dense"] * 1e3,
                   "tflops": flop_dense / per["dense"] / 1e9,
@@ -149,7 +153,8 @@ def main():
                 "speedup_vs_dense": per["dense"] / t_gsa,
                 "kernels_ms": {n[4:]: per[n] for n in names if n.startswith("gsa_")},
                 "compressed_tflops": flop_cmp / per["gsa_compressed"] / 1e9,
-                "compressed_mfma_frac": flop_cmp / per["gsa_compressed"] / 1e9 / PEAK_BF16_TFLOPS},
+                "compressed_mfma_frac": flop_cmp / per["gsa_compressed"] / 1e9 / PEAK_BF16_TFLOPS,
+                "kernels_roofline": gsa_roof},
         "subsampled": {"ms": per["sga"], "tokens_per_s": T / per["sga"] * 1e3,
                        "speedup_vs_dense": per["dense"] / per["sga"],
                        "tflops": flop_sga / per["sga"] / 1e9,
@@ -183,6 +188,40 @@ def main():
         "layers": layers, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+PEAK_HBM_GBS = 8000.0
+
+
+def gsa_rooflines(geom, wl, per, idx):
+    """Per-step roofline of the GSA kernels from their timed durations:
+    algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call."""
+    import torch
+    T, H, d, N, S = geom.n_tokens, geom.n_heads, geom.head_dim, geom.n_frames, geom.n_special
+    nbh, nbw = -(-geom.grid_h // 4), -(-geom.grid_w // 4)
+    nb = nbh * nbw
+    nqb = nb + (1 if S else 0)
+    # tokens per 4x4 window (edge windows are clipped to the grid)
+    rows = torch.tensor([min(4, geom.grid_h - 4 * by) for by in range(nbh)])
+    cols = torch.tensor([min(4, geom.grid_w - 4 * bx) for bx in range(nbw)])
+    win = (rows[:, None] * cols[None, :]).reshape(-1).to(idx.device)
+    qcount = torch.cat([win, torch.tensor([S], device=idx.device)])[:nqb] if S else win
+    sel = win[(idx.long() % nb)].sum(dim=2)                   # [H, N*nqb] keys chosen
+    per_block = qcount.repeat(N)[None, :].double()            # queries per block
+    pairs = float((per_block * (sel.double() + N * S)).sum())  # (query, key) pairs, all heads
+    out = {}
+    pool_bytes = 3 * T * H * d * 2 + N * nb * H * d * (2 + 2 + 4) + N * nqb * H * d * 4
+    gate_bytes = 4 * T * H * d * 2
+    flops = {"compressed": 4.0 * T * N * nb * d * H,
+             "topk": 3 * 2.0 * d * (N * nqb) * (N * nb) * H,  # three bf16 products per score
+             "fine": 4.0 * d * pairs}
+    for name, nbytes in (("pool", pool_bytes), ("gate", gate_bytes)):
+        gbs = nbytes / (per["gsa_" + name] * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "gb_per_s": gbs, "frac": gbs / PEAK_HBM_GBS, "bytes": nbytes}
+    for name, fl in flops.items():
+        tf = fl / (per["gsa_" + name] * 1e-3) / 1e12
+        out[name] = {"bound": "mfma", "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS, "flop": fl}
+    return out
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "flash_dense_scene1000_traffic.json")

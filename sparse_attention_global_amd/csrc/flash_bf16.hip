@@ -44,11 +44,29 @@
 namespace sga {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;         // 128 queries per workgroup
-constexpr int kRowsPerWave = 64 / kWaves;    // K rows and V^T rows each wave fetches per tile
-constexpr int kLoadsPerTile = 2 * kRowsPerWave / 8;  // 16-byte direct loads per lane per tile
+enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
+
+// Tiling per mode: waves per workgroup (32 queries each), workgroups per CU,
+// LDS ring stages (16 KiB each), and how many waves issue the tile loads
+// (64 K rows + 64 V^T rows of 128 B per tile, spread evenly over them).
+// Measured for dense attention at 128 frames (% of bf16 peak): 4 waves x 3
+// workgroups x 3 stages 46.6; 12 x 1 x 3 (8 loading) 45.6; 8 x 1 x 5 43.2;
+// 6 x 2 x 3 38.8 (the register budget then allows only 2 waves per SIMD).
+template <int W, int G, int S, int D>
+struct TileCfg {
+  static constexpr int waves = W;
+  static constexpr int wg_per_cu = G;
+  static constexpr int stages = S;
+  static constexpr int dma_waves = D;
+  static constexpr int threads = W * 64;
+  static constexpr int block_m = W * 32;
+  static constexpr int rows_per_wave = 64 / D;           // K rows and V^T rows per loading wave
+  static constexpr int loads_per_tile = 2 * rows_per_wave / 8;  // 16-byte loads per lane
+  static_assert(D <= W && 64 % D == 0 && rows_per_wave % 8 == 0, "load split");
+  static_assert(S >= 2 && S <= 9, "ring");
+};
+template <int MODE>
+struct Cfg : TileCfg<4, 3, 3, 4> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -61,16 +79,11 @@ constexpr float kLooseBoundSum = 8.271806125530277e-25f;  // 2^-80
 // Occupancy: 3 workgroups (12 waves) per CU with a 3-stage LDS ring (144 KiB).
 // Measured on MI355X at 128 frames (dense attention, % of bf16 peak): 3 stages
 // and 3 workgroups 44-46%; 2 / 3 43%; 2 / 4, where the 128-VGPR budget makes the
-// compiler spill inside the tile loop, 37%; 8-wave workgroups sharing each tile
-// (2 waves per SIMD) 44%. A ping-pong schedule of two barrier-locked wave groups
-// per SIMD (one group on MFMA while the other computes probabilities) reached
-// only 30-39%: the per-phase barriers, LDS waits and scalar work cost more than
-// the forced overlap gains, where three free-running waves per SIMD overlap
-// MFMA and VALU work by themselves.
-constexpr int kStages = 3;
-constexpr int kWgPerCu = 3;
-
-enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
+// compiler spill inside the tile loop, 37%. A ping-pong schedule of two
+// barrier-locked wave groups per SIMD (one group on MFMA while the other
+// computes probabilities) reached only 30-39%: the per-phase barriers, LDS
+// waits and scalar work cost more than the forced overlap gains, where three
+// free-running waves per SIMD overlap MFMA and VALU work by themselves.
 
 struct FlashArgs {
   const bf16* q;
@@ -126,8 +139,9 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // every wave is done reading the stage about to be refilled.
 template <int N>
 __device__ __forceinline__ void wait_and_meet() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // vmcnt <= N; lgkmcnt, expcnt unconstrained
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // vmcnt <= N (bits 3:0 and 15:14); lgkmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -137,9 +151,15 @@ __device__ __forceinline__ void wait_and_meet() {
 // in A.redo whether some row's probabilities underflowed. EXACT = true: only the
 // recorded workgroups run, redoing their rows with the exact online softmax.
 template <int MODE, bool EXACT>
-__global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArgs A) {
+__global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flash_bf16_kernel(
+    FlashArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  using C = Cfg<MODE>;
+  constexpr int kStages = C::stages;
   constexpr int kAhead = kStages - 1;  // tiles in flight ahead of the one consumed
+  constexpr int kBlockM = C::block_m;
+  constexpr int kRowsPerWave = C::rows_per_wave;
+  constexpr int kLoadsPerTile = C::loads_per_tile;
 
   int lid = blockIdx.x;
   if (A.remap) {
@@ -214,6 +234,7 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
                                 kHeadDim * sg.vt_ld * 2);
     unsigned char* kdst = stage + wave_u * kRowsPerWave * 128;
     unsigned char* vdst = kdst + kTileKBytes;
+    if (C::dma_waves < C::waves && wave_u >= C::dma_waves) return;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave / 8; ++i) {
       lds_dma16(kr, k_off[i], kdst + 8 * i * 128);
@@ -292,16 +313,23 @@ __global__ __launch_bounds__(kThreads, kWgPerCu) void flash_bf16_kernel(FlashArg
 
   // The tile loop: a ring of kStages LDS stages, kAhead tiles in flight, in
   // the order tile_of(0), tile_of(1), ...
-  static_assert(kStages == 3, "the main loop is written for a 3-stage ring");
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
     if (j < n_tiles) issue_tile(tile_of(j), smem + j * kStageBytes);
   // wait for tile j (the tiles after it in flight: min(kAhead - 1, left)), meet
   // the other waves (all done with tile j - 1's stage), refill that stage
+  // (waves that issue no loads have nothing outstanding: every wait passes)
   auto enter = [&](long long j, unsigned char* refill_stage) {
     const long long left = n_tiles - 1 - j;
     if (left >= kAhead - 1) {
       wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
+    } else if (kAhead > 2 && left == kAhead - 2) {
+      wait_and_meet<(kAhead > 2 ? kAhead - 2 : 0) * kLoadsPerTile>();
+    } else if (kAhead > 3 && left == kAhead - 3) {
+      wait_and_meet<(kAhead > 3 ? kAhead - 3 : 0) * kLoadsPerTile>();
+    } else if (left > 0) {
+      // (deeper rings: wait for everything rather than track each count)
+      wait_and_meet<0>();
     } else {
       wait_and_meet<0>();
     }
@@ -426,9 +454,13 @@ static long long vt_ld_compact(const FlashLaunch& p) {
   if (p.mode != FLASH_SUBSAMPLED) return 0;
   return ((long long)p.g.n_frames * (p.mk + p.has_mean) + 63) / 64 * 64;
 }
+static int block_m(int mode) {
+  return mode == FLASH_GLOBAL ? Cfg<MODE_GLOBAL>::block_m : Cfg<MODE_FRAME>::block_m;
+}
 static long long logical_workgroups(const FlashLaunch& p) {
-  if (p.mode == FLASH_GLOBAL) return (p.g.T + kBlockM - 1) / kBlockM * p.g.n_heads;
-  return (long long)((p.g.L + kBlockM - 1) / kBlockM) * p.g.n_frames * p.g.n_heads;
+  const int bm = block_m(p.mode);
+  if (p.mode == FLASH_GLOBAL) return (p.g.T + bm - 1) / bm * p.g.n_heads;
+  return (long long)((p.g.L + bm - 1) / bm) * p.g.n_frames * p.g.n_heads;
 }
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -478,7 +510,7 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   if (p.mode == FLASH_GLOBAL) {
     e = launch_vt_prepare(p.v, p.g.n_heads, p.n_keys, p.n_keys, A.vt_ld, A.vt_ld, vt, stream);
     if (e != hipSuccess) return e;
-    A.n_qtiles = (int)((p.g.T + kBlockM - 1) / kBlockM);
+    A.n_qtiles = (int)((p.g.T + block_m(p.mode) - 1) / block_m(p.mode));
     A.remap = 0;
   } else {
     A.vt_pitch = (p.g.L + 63) / 64 * 64;
@@ -492,7 +524,7 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
       if (e != hipSuccess) return e;
       A.cvt = cvt;
     }
-    A.n_qtiles = (p.g.L + kBlockM - 1) / kBlockM;
+    A.n_qtiles = (p.g.L + block_m(p.mode) - 1) / block_m(p.mode);
     A.remap = 1;
   }
   // key-norm partials over every key the queries can meet (the compacted
@@ -507,21 +539,22 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   A.n_logical = (int)logical_workgroups(p);
   const int grid = A.remap ? ((A.n_logical + 7) / 8) * 8 : A.n_logical;
   // the main pass, then the exact pass over the workgroups it flagged
-  auto launch = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kStages * kStageBytes, stream, A);
+  auto launch = [&](auto kernel, auto cfg) {
+    using C = decltype(cfg);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::threads), C::stages * kStageBytes, stream, A);
   };
   switch (p.mode) {
     case FLASH_GLOBAL:
-      launch(flash_bf16_kernel<MODE_GLOBAL, false>);
-      launch(flash_bf16_kernel<MODE_GLOBAL, true>);
+      launch(flash_bf16_kernel<MODE_GLOBAL, false>, Cfg<MODE_GLOBAL>{});
+      launch(flash_bf16_kernel<MODE_GLOBAL, true>, Cfg<MODE_GLOBAL>{});
       break;
     case FLASH_FRAME:
-      launch(flash_bf16_kernel<MODE_FRAME, false>);
-      launch(flash_bf16_kernel<MODE_FRAME, true>);
+      launch(flash_bf16_kernel<MODE_FRAME, false>, Cfg<MODE_FRAME>{});
+      launch(flash_bf16_kernel<MODE_FRAME, true>, Cfg<MODE_FRAME>{});
       break;
     default:
-      launch(flash_bf16_kernel<MODE_SUBSAMPLED, false>);
-      launch(flash_bf16_kernel<MODE_SUBSAMPLED, true>);
+      launch(flash_bf16_kernel<MODE_SUBSAMPLED, false>, Cfg<MODE_SUBSAMPLED>{});
+      launch(flash_bf16_kernel<MODE_SUBSAMPLED, true>, Cfg<MODE_SUBSAMPLED>{});
       break;
   }
   return hipGetLastError();
