@@ -234,6 +234,27 @@ def test_topk_planted_winners():
             assert np.array_equal(got[h, bb], want), (h, bb)
 
 
+@pytest.mark.parametrize("top_k", [7, 16, 32, 128])
+def test_topk_widths(top_k):
+    """Both selection kernels: register lists up to 16, LDS lists beyond."""
+    geom = Geometry(16, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"top-K width {top_k} {geom}")
+    q, k, v = make_qkv(geom, seed=31, device=DEV, distribution="scene")
+    _, _, k32, q32 = sga.gsa_compress(q, k, v, geom)
+    idx, score = sga.gsa_select_topk(q32, k32, geom, top_k, want_score=True)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    rkc, _ = oracle.compress(kh, vh, geom, 4)
+    rqb = oracle.pooled_queries(qh, geom, 4)
+    ridx, ranked = oracle.select_topk(rqb, rkc, top_k)
+    check_topk(host(idx).astype(np.int64), ridx, ranked, rqb, rkc, f"top-{top_k}")
+    idx_h = host(idx).astype(np.int64)
+    s_h = host(score)
+    for h in range(geom.n_heads):
+        ref = np.einsum("bkd,bd->bk", rkc[idx_h[h], h, :], rqb[:, h, :]) / 8.0
+        assert np.max(np.abs(s_h[h] - ref)) < 1e-4
+
+
 def test_deterministic():
     geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
     _announce(f"determinism {geom}")
