@@ -78,6 +78,8 @@ def main():
     q, k, v = make_qkv(geom, seed=args.seed, device=dev, distribution=wl.distribution)
     w, b = make_gate(H, d, seed=args.seed, device=dev)
     ws = torch.empty(sga.workspace_bytes(geom, sh, sw, sga.SGA_BF16), dtype=torch.uint8, device=dev)
+    ws_fine = torch.empty(sga.fine_workspace_bytes(geom, sga.SGA_BF16, True), dtype=torch.uint8,
+                          device=dev)
     torch.cuda.synchronize()
     print(f"[bench] inputs ready: {args.workload} T={T} H={H} d={d}", file=sys.stderr, flush=True)
 
@@ -100,7 +102,7 @@ def main():
         idx = sga.gsa_select_topk(q32, k32, geom, wl.top_k)
         last["idx"] = idx
         ev[i].record(); i += 1
-        o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, wl.top_k)
+        o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, wl.top_k, ws=ws_fine)
         ev[i].record(); i += 1
         sga.gsa_gate(q, o_cmp, o_slc, w, b, geom)
         ev[i].record(); i += 1

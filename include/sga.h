@@ -111,14 +111,20 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
  * query block b attends to the in-grid tokens of the pooled blocks listed in
  * idx[h, b, :] and, when keep_special == 1, to every special token of every
  * frame (the camera tokens kept by the VGGT adaptation in the Italian summary;
- * special tokens kept in AVGGT section 2.2).
+ * special tokens kept in AVGGT section 2.2). One softmax over the union.
  * idx: [H, N*nqb, top_k] int32 entries in [0, N*nb), distinct within a row.
  * o_slc: [T, H, d]. lse (nullable): [T, H] fp32.
+ * ws: sga_workspace_size(geom, SGA_OP_FINE, keep_special, 0, &bytes) bytes.
+ *   bf16 with keep_special == 1 and n_special > 0: the special tokens' keys and
+ *   values gathered contiguously, the log-sum-exp of every query over them,
+ *   and the dense kernel's staging for them (the special part runs through the
+ *   dense attention kernel, the selected windows then continue its softmax).
+ *   Otherwise 0 bytes and ws may be NULL.
  */
 sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q,
                            const void* k, const void* v, const int32_t* idx,
                            int32_t top_k, int32_t keep_special, void* o_slc,
-                           float* lse, void* stream);
+                           float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * GSA gated aggregation (Speed3R section 2.1; Italian summary section 2):
@@ -158,11 +164,12 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
                                   const void* k, const void* v, void* o, void* ws,
                                   size_t ws_bytes, void* stream);
 
-enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2 };
+enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3 };
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
- * stride_h, stride_w (covers both modes). */
+ * stride_h, stride_w (covers both modes). SGA_OP_FINE: param0 = keep_special,
+ * param1 unused (0). */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

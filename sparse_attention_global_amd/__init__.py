@@ -1,7 +1,8 @@
 """MI355X-native global cross-frame attention layer (dense, Speed3R GSA, AVGGT
 subsampled) -- Python binding of the HIP library libsga.so."""
 from ._lib import (  # noqa: F401
-    EXPORTS, SGA_BF16, SGA_F32, compact_rows, dense_global_attn, dense_workspace_bytes, gsa_compress, gsa_gate,
+    EXPORTS, SGA_BF16, SGA_F32, compact_rows, dense_global_attn, dense_workspace_bytes,
+    fine_workspace_bytes, gsa_compress, gsa_gate,
     gsa_layer, gsa_select_topk, gsa_sparse_attn, library, pooled_shape, sga_compact,
     subsampled_global_attn, tokens, workspace_bytes,
 )

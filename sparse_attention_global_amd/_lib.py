@@ -20,6 +20,7 @@ _lib = None
 SGA_BF16, SGA_F32 = 0, 1
 SGA_OP_SUBSAMPLED = 1
 SGA_OP_DENSE = 2
+SGA_OP_FINE = 3
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_select_topk", "gsa_sparse_attn", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
@@ -47,7 +48,7 @@ def library() -> ctypes.CDLL:
         "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
         "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
         "gsa_select_topk": [G, I32, P, P, I32, P, P, P],
-        "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P],
+        "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
         "sga_compact": [G, I32, I32, P, P, P, P, P],
         "subsampled_global_attn": [G, I32, I32, I32, I32, P, P, P, P, P, SZ, P],
@@ -189,8 +190,16 @@ def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
     return (idx, score) if want_score else idx
 
 
+def fine_workspace_bytes(geom, dtype_code: int, keep_special: bool = True) -> int:
+    n = ctypes.c_size_t(0)
+    g = make_geom(geom, dtype_code)
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_FINE, int(keep_special), 0,
+                                        ctypes.byref(n)), "sga_workspace_size")
+    return n.value
+
+
 def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, block: int = 4,
-                    want_lse: bool = False):
+                    want_lse: bool = False, ws=None):
     """Fine attention over the selected blocks (+ all special tokens); see include/sga.h."""
     T, H, d, N = tokens(geom), geom.n_heads, 64, geom.n_frames
     nb, nqb = pooled_shape(geom, block)
@@ -201,9 +210,13 @@ def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, b
         raise ValueError(f"idx must be a contiguous int32 tensor of shape {(H, N * nqb, top_k)}")
     o = torch.empty_like(q)
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if want_lse else None
-    g = make_geom(geom, _dtype_code(q))
+    code = _dtype_code(q)
+    g = make_geom(geom, code)
+    ws = _workspace(fine_workspace_bytes(geom, code, keep_special), q.device, ws)
     _check(library().gsa_sparse_attn(ctypes.byref(g), block, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                     top_k, int(keep_special), _ptr(o), _ptr(lse), _stream(q)),
+                                     top_k, int(keep_special), _ptr(o), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(q)),
            "gsa_sparse_attn")
     return (o, lse) if want_lse else o
 

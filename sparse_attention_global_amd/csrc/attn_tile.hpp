@@ -116,6 +116,25 @@ struct WaveAttnState {
     l = 0.f;
   }
 
+  // Start from a normalised partial result: orow is the query's output over
+  // some keys (bf16 [d]) and lse their log-sum-exp in natural-log units of the
+  // scaled logits; it then counts as one key of logit lse and value orow.
+  __device__ __forceinline__ void init_from(const bf16* orow, float lse) {
+    const int hh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(orow + db * 32 + 8 * g4 + 4 * hh);
+        oacc[db][4 * g4 + 0] = lo_bf16(w[0]);
+        oacc[db][4 * g4 + 1] = hi_bf16(w[0]);
+        oacc[db][4 * g4 + 2] = lo_bf16(w[1]);
+        oacc[db][4 * g4 + 3] = hi_bf16(w[1]);
+      }
+    m = lse * 8.f;  // raw logit units: the logits here are q.k, scaled by 1/sqrt(64) = 1/8
+    l = 0.5f;       // each half-wave holds half of the sum, 1
+  }
+
   // Scores of one 64-key tile: S^T = K Q^T for two 32-key blocks.
   __device__ __forceinline__ void scores(const unsigned char* stage, const TileLaneOffsets& off,
                                          const u32x4 qB[4], f32x16 s[2]) const {

@@ -98,13 +98,19 @@ void compact_shape(const sga::Geom& g, int s_h, int s_w, int* mk, int* has_mean,
 
 size_t elt_size(const sga_geom* g) { return g->dtype == SGA_BF16 ? 2 : 4; }
 
-// FlashLaunch of a dense_global_attn call (validated geometry and keys).
 sga_status check_fits(const sga::FlashLaunch& p) {
   if (!sga::flash_bf16_fits(p))
     return fail(SGA_ERR_UNSUPPORTED, "too many keys or heads for the bf16 kernel's 31-bit tile extents");
   return SGA_OK;
 }
 
+// gsa_sparse_attn workspace (bf16 with specials): gathered K and V of the
+// N*S special tokens, the queries' log-sum-exp over them, the dense staging.
+struct FineLayout {
+  long long rows = 0;
+  size_t kv = 0, lse = 0, flash = 0, total = 0;
+};
+// FlashLaunch of a dense_global_attn call (validated geometry and keys).
 sga::FlashLaunch dense_launch(const sga::Geom& g, int64_t n_keys, int32_t frame_local) {
   sga::FlashLaunch p{};
   p.g = g;
@@ -114,6 +120,18 @@ sga::FlashLaunch dense_launch(const sga::Geom& g, int64_t n_keys, int32_t frame_
 }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+FineLayout fine_layout(const sga::Geom& g, bool bf, int keep_special) {
+  FineLayout lay;
+  lay.rows = (long long)g.n_frames * g.n_special;
+  if (!bf || !keep_special || lay.rows == 0) return lay;
+  lay.kv = round256((size_t)lay.rows * g.n_heads * sga::kHeadDim * 2);
+  lay.lse = round256((size_t)g.T * g.n_heads * sizeof(float));
+  lay.flash = round256(sga::flash_bf16_workspace(dense_launch(g, lay.rows, 0)));
+  lay.total = 2 * lay.kv + lay.lse + lay.flash;
+  return lay;
+}
+
 
 // Workspace layout of subsampled_global_attn (bf16 and fp32): compacted keys,
 // compacted values, then (bf16) the attention kernel's V^T staging.
@@ -204,7 +222,7 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
 
 sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
                            const void* v, const int32_t* idx, int32_t top_k, int32_t keep_special,
-                           void* o_slc, float* lse, void* stream) {
+                           void* o_slc, float* lse, void* ws, size_t ws_bytes, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
@@ -216,8 +234,37 @@ sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, c
   REQUIRE_PTR(o_slc);
   REQUIRE_OPT_PTR(lse);
   if (keep_special != 0 && keep_special != 1) return fail(SGA_ERR_INVALID_ARG, "keep_special must be 0 or 1");
-  return from_hip(sga::launch_gsa_fine(g, geom->dtype == SGA_BF16, q, k, v, idx, top_k, keep_special,
-                                       o_slc, lse, static_cast<hipStream_t>(stream)),
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf = geom->dtype == SGA_BF16;
+  const FineLayout lay = fine_layout(g, bf, keep_special);
+  if (lay.total == 0)
+    return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep_special, o_slc, lse,
+                                         nullptr, nullptr, s),
+                    "gsa_sparse_attn launch");
+  if (ws == nullptr || ws_bytes < lay.total)
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                ws == nullptr ? 0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  // the special tokens of every frame through the dense kernel: o_slc and the
+  // log-sum-exp hold that partial result, which the window kernel continues
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  void* k_s = w;
+  void* v_s = w + lay.kv;
+  float* lse_s = reinterpret_cast<float*>(w + 2 * lay.kv);
+  void* flash_ws = w + 2 * lay.kv + lay.lse;
+  if (hipError_t e = sga::launch_gather_specials(g, k, v, k_s, v_s, s))
+    return from_hip(e, "gsa_sparse_attn (specials) launch");
+  sga::FlashLaunch p = dense_launch(g, lay.rows, 0);
+  p.q = q;
+  p.k = k_s;
+  p.v = v_s;
+  p.o = o_slc;
+  p.lse = lse_s;
+  if (sga_status st = check_fits(p)) return st;
+  if (hipError_t e = sga::launch_flash_bf16(p, flash_ws, s))
+    return from_hip(e, "gsa_sparse_attn (specials attention) launch");
+  return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, 0, o_slc, lse,
+                                       static_cast<const sga::bf16*>(o_slc), lse_s, s),
                   "gsa_sparse_attn launch");
 }
 
@@ -259,6 +306,12 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
     if (param0 < 0 || (param1 != 0 && param1 != 1) || (param1 && param0 != 0))
       return fail(SGA_ERR_INVALID_ARG, "dense workspace: n_keys >= 0, frame_local 0/1 (n_keys 0 if 1)");
     *bytes = geom->dtype == SGA_BF16 ? sga::flash_bf16_workspace(dense_launch(g, param0, param1)) : 0;
+    return SGA_OK;
+  }
+  if (op == SGA_OP_FINE) {
+    if ((param0 != 0 && param0 != 1) || param1 != 0)
+      return fail(SGA_ERR_INVALID_ARG, "fine workspace: param0 = keep_special (0/1), param1 = 0");
+    *bytes = fine_layout(g, geom->dtype == SGA_BF16, param0).total;
     return SGA_OK;
   }
   if (op != SGA_OP_SUBSAMPLED) return fail(SGA_ERR_INVALID_ARG, "unknown op %d", op);
@@ -329,6 +382,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 100; }
+int32_t sga_version(void) { return 20000; }
 
 }  // extern "C"

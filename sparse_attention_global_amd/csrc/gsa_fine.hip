@@ -4,18 +4,20 @@
 // (kept whole: the camera tokens of the VGGT adaptation in the Italian summary;
 // the special tokens of AVGGT section 2.2).
 //
-// Work split (bf16): a workgroup of 4 waves owns 8 consecutive query blocks of
-// one head; each wave owns two of them as the 32 MFMA columns (block b0 in
-// columns 0..15, block b0 + 1 in columns 16..31, member m of a 4x4 window at
-// grid offset (m / 4, m % 4); a specials block holds its S tokens).
-//   Phase 1 -- the special tokens are the same keys for every query: they
-//   stream through LDS once per workgroup, double buffered, exactly as in the
-//   dense kernel.
-//   Phase 2 -- each wave gathers its own blocks' selected tokens (top_k windows
-//   x 16 slots, 64 keys = 4 windows per tile) into a private LDS stage; while
-//   one block's keys are processed the other block's 16 columns sit out.
-// Both phases feed the same per-wave online-softmax state, so the result is one
-// softmax over the union of the key sets.
+// bf16: the special tokens are the same keys for every query, so that part is
+// dense attention over N*S keys: the C ABI gathers them and runs the dense
+// kernel, which leaves every query's normalised partial output and its
+// log-sum-exp. This kernel then starts each query's online softmax from that
+// partial result (as one pre-merged key: logit = its log-sum-exp, value = its
+// output) and adds the selected windows, so the result is one softmax over
+// the union of the key sets.
+// Work split: a workgroup of 4 waves owns 8 consecutive query blocks of one
+// head; each wave owns two of them as the 32 MFMA columns (block b0 in columns
+// 0..15, block b0 + 1 in columns 16..31, member m of a 4x4 window at grid
+// offset (m / 4, m % 4); a specials block holds its S tokens). Each wave
+// gathers its own blocks' selected tokens (top_k windows x 16 slots, 64 keys =
+// 4 windows per tile) into a private LDS stage; while one block's keys are
+// processed the other block's 16 columns sit out.
 #include "attn_tile.hpp"
 #include "kernels.hpp"
 
@@ -33,9 +35,11 @@ struct FineArgs {
   const int32_t* idx;  // [H, N*nqb, top_k]
   bf16* o;
   float* lse;
+  const bf16* o_init;     // nullable: partial result each query starts from
+  const float* lse_init;  // its log-sum-exp (natural log of the scaled logits)
   Geom g;
   int top_k;
-  int keep_special;
+  int keep_special;  // (bf16: 0; the special tokens arrive through o_init)
   int n_wg_per_head;
   float c;
 };
@@ -82,53 +86,14 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
 
   WaveAttnState st;
   st.init();
+  if (A.o_init != nullptr && qvalid) {
+    st.init_from(A.o_init + qrow * rs + hoff, A.lse_init[qrow * g.n_heads + h]);
+  }
   TileLaneOffsets off;
   off.init();
   const float c = A.c;
 
-  // ---- phase 1: all special tokens, shared through LDS ----------------------
-  const long long n_spec = A.keep_special ? (long long)g.n_frames * g.n_special : 0;
-  if (n_spec > 0) {
-    const int ld_key = 2 * (tid >> 3), ld_chunk = tid & 7;
-    u32x4 kreg[2], vreg[2];
-    auto load_tile = [&](long long u0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const long long u = u0 + ld_key + i;
-        if (u < n_spec) {
-          const long long row = (u / g.n_special) * g.L + (u % g.n_special);
-          kreg[i] = ld16(A.k + row * rs + hoff + ld_chunk * 8);
-          vreg[i] = ld16(A.v + row * rs + hoff + ld_chunk * 8);
-        } else {
-          kreg[i] = u32x4{0, 0, 0, 0};
-          vreg[i] = u32x4{0, 0, 0, 0};
-        }
-      }
-    };
-    auto store_tile = [&](int stage, long long u0) {
-      unsigned char* sp = smem + stage * kTileStageBytes;
-      tile_store_kv_pair(sp, ld_key, ld_chunk, kreg[0], kreg[1], vreg[0], vreg[1]);
-      if (ld_chunk == 0) {
-        tile_bias(sp)[ld_key] = (u0 + ld_key < n_spec) ? 0.f : -INFINITY;
-        tile_bias(sp)[ld_key + 1] = (u0 + ld_key + 1 < n_spec) ? 0.f : -INFINITY;
-      }
-    };
-    const long long n_tiles = (n_spec + kTileKeys - 1) / kTileKeys;
-    load_tile(0);
-    store_tile(0, 0);
-    __syncthreads();
-    for (long long it = 0; it < n_tiles; ++it) {
-      const int stage = (int)(it & 1);
-      const long long u0 = it * kTileKeys;
-      const bool more = it + 1 < n_tiles;
-      if (more) load_tile(u0 + kTileKeys);
-      st.step(smem + stage * kTileStageBytes, off, qB, c, u0 + kTileKeys > n_spec, true);
-      if (more) store_tile(stage ^ 1, u0 + kTileKeys);
-      __syncthreads();
-    }
-  }
-
-  // ---- phase 2: each wave's selected windows, private LDS stage --------------
+  // ---- each wave's selected windows, private LDS stage -----------------------
   unsigned char* my_stage = smem + wave * kTileStageBytes;
   const int n_t2 = (A.top_k + 3) / 4;
   for (int sd = 0; sd < 2; ++sd) {
@@ -225,11 +190,40 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
   if (lse) lse[t * g.n_heads + h] = m + logf(l);
 }
 
+// k_s[u] = k[row of special token u] (u = f * S + s), likewise v: a thread per
+// 16-byte chunk.
+__global__ __launch_bounds__(256) void gather_specials_kernel(Geom g, const u32x4* __restrict__ k,
+                                                              const u32x4* __restrict__ v,
+                                                              u32x4* __restrict__ k_s,
+                                                              u32x4* __restrict__ v_s) {
+  const long long chunks_per_row = (long long)g.n_heads * kHeadDim / 8;
+  const long long n = (long long)g.n_frames * g.n_special * chunks_per_row;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const long long u = i / chunks_per_row, ch = i % chunks_per_row;
+  const long long row = (u / g.n_special) * g.L + (u % g.n_special);
+  k_s[i] = k[row * chunks_per_row + ch];
+  v_s[i] = v[row * chunks_per_row + ch];
+}
+
 }  // namespace
+
+hipError_t launch_gather_specials(const Geom& g, const void* k, const void* v, void* k_s,
+                                  void* v_s, hipStream_t stream) {
+  const long long n = (long long)g.n_frames * g.n_special * g.n_heads * kHeadDim / 8;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_specials_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g,
+                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                     static_cast<u32x4*>(k_s), static_cast<u32x4*>(v_s));
+  return hipGetLastError();
+}
 
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
                            const void* v, const int32_t* idx, int top_k, int keep_special,
-                           void* o, float* lse, hipStream_t stream) {
+                           void* o, float* lse, const bf16* o_init, const float* lse_init,
+                           hipStream_t stream) {
   if (!is_bf16) {
     dim3 grid((unsigned)((g.T + 63) / 64), (unsigned)g.n_heads);
     hipLaunchKernelGGL(gsa_fine_f32_kernel, grid, dim3(64), 0, stream, g,
@@ -238,6 +232,8 @@ hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const voi
                        static_cast<float*>(o), lse);
     return hipGetLastError();
   }
+  // bf16: the special tokens come in through o_init / lse_init only
+  if (keep_special && g.n_special > 0) return hipErrorInvalidValue;
   FineArgs A{};
   A.q = static_cast<const bf16*>(q);
   A.k = static_cast<const bf16*>(k);
@@ -248,6 +244,8 @@ hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const voi
   A.g = g;
   A.top_k = top_k;
   A.keep_special = keep_special;
+  A.o_init = o_init;
+  A.lse_init = lse_init;
   A.c = kLog2e / sqrtf((float)kHeadDim);
   const long long n_qb = (long long)g.n_frames * g.nqb;
   A.n_wg_per_head = (int)((n_qb + kBlocksPerWG - 1) / kBlocksPerWG);

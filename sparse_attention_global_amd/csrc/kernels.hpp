@@ -52,10 +52,18 @@ hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const voi
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
                            int32_t* idx, float* score, hipStream_t stream);
 
-// GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32.
+// GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32. With o_init/lse_init
+// (bf16 only) every query's softmax starts from that partial result (the
+// attention over the special tokens, normalised, and its log-sum-exp) and the
+// selected windows continue it; keep_special must then be 0.
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
                            const void* v, const int32_t* idx, int top_k, int keep_special,
-                           void* o, float* lse, hipStream_t stream);
+                           void* o, float* lse, const bf16* o_init, const float* lse_init,
+                           hipStream_t stream);
+// The N*S special tokens' keys and values, gathered contiguously (frame-major,
+// [N*S, H, d]) for the dense kernel (gsa_fine.hip).
+hipError_t launch_gather_specials(const Geom& g, const void* k, const void* v, void* k_s,
+                                  void* v_s, hipStream_t stream);
 
 // GSA gate (gsa_gate.hip).
 hipError_t launch_gsa_gate(const Geom& g, bool is_bf16, const void* q, const void* o_cmp,

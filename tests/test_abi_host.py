@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 100
+    assert library().sga_version() == 20000
 
 
 def geom(**kw):
@@ -91,7 +91,8 @@ def test_gsa_calls_reject_bad_arguments():
     for bad_k in (0, nb + 1, 129):
         assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, FAKE, None, None) == INVALID
         assert "top_k" in last_error()
-    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 2, FAKE, None, None) == INVALID
+    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 2, FAKE, None, None, 0,
+                             None) == INVALID
     assert "keep_special" in last_error()
     assert L.gsa_gate(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
 
@@ -145,6 +146,28 @@ def test_workspace_sizes():
     assert _ws(g1, 1, 1, 1) == (OK, 2 * r256(3 * (5 + 37 * 37) * 16 * 64 * 4))
     assert _ws(g1, 2, 0, 0) == (OK, 0)
     assert _ws(g1, 7, 1, 1)[0] == INVALID
+
+
+def test_fine_workspace():
+    g = geom(n_frames=256)
+    T = 256 * 1374
+    # bf16 with the special tokens: their gathered K and V (256 frames x 5), the
+    # queries' log-sum-exp over them, and the dense staging for 1280 keys
+    # (V^T, key-norm partials, one redo flag per 128-query workgroup)
+    kv = r256(1280 * 16 * 64 * 2)
+    lse = r256(T * 16 * 4)
+    flash = r256(16 * 64 * 1280 * 2 + 16 * 256 * 4 + r256(-(-T // 128) * 16))
+    assert _ws(g, 3, 1, 0) == (OK, 2 * kv + lse + flash)
+    assert _ws(g, 3, 0, 0) == (OK, 0)
+    assert _ws(geom(n_frames=4, n_special=0), 3, 1, 0) == (OK, 0)
+    assert _ws(geom(n_frames=4, dtype=1), 3, 1, 0) == (OK, 0)
+    assert _ws(g, 3, 2, 0)[0] == INVALID
+    assert _ws(g, 3, 1, 7)[0] == INVALID
+    # a missing workspace is reported before anything is launched
+    L = library()
+    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, None,
+                             None, 0, None) == WORKSPACE
+    assert "workspace" in last_error()
 
 
 def test_python_layer_requires_gpu_tensors():
