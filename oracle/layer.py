@@ -40,7 +40,13 @@ R10 a patch (r, c) is kept iff r % s_h == 0 and c % s_w == 0;
 R11 one mean key/value per *other* frame, the plain mean of that frame's
     dropped patches, entering the softmax as one ordinary key (optionally with
     log(#dropped) added to its logit); omitted when nothing is dropped;
-R12 token order inside a frame: special tokens first, then patches row-major.
+R12 token order inside a frame: special tokens first, then patches row-major;
+R13 the VGGT adaptation of the selection branch ([Speed3R-ja] section 2.2,
+    architecture adaptation; [Speed3R-it] section 2) keeps the reference frame
+    -- frame 0, whose camera fixes VGGT's world coordinates -- whole: every
+    query's fine branch attends to all tokens of frame 0, and the top-K is
+    taken over the pooled blocks of the other frames only, so that no token is
+    counted twice.
 
 Arrays are ``[rows, H, d]`` of any float dtype; every computation widens them
 to fp64 first.
@@ -270,19 +276,21 @@ def block_scores(q_blk, k_cmp):
     return np.einsum("bhd,jhd->hbj", qb, kc) / math.sqrt(d)
 
 
-def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None):
+def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None, first: int = 0):
     """Top-K pooled blocks per (head, query block) from the compressed scores
     ([Speed3R-ja] section 2.1, selection branch, first bullet; [Speed3R-it]
     section 2, "Ramo di Selezione"). Order: larger score first, ties to the
     lower block index (R6). Returns (idx [H, n, K] int32 ascending,
     ranked [H, n, K+1] fp64 = the K+1 best scores in rank order, +-inf padded).
+    Only pooled keys j >= ``first`` compete (R13: ``first`` = the reference
+    frame's block count); the returned indices are global.
     """
     qb = np.asarray(q_blk, dtype=np.float64)
-    kc = np.asarray(k_cmp, dtype=np.float64)
+    kc = np.asarray(k_cmp, dtype=np.float64)[first:]
     n, H, d = qb.shape
     nk = kc.shape[0]
     if not 1 <= top_k <= nk:
-        raise ValueError("top_k must lie in [1, number of pooled keys]")
+        raise ValueError("top_k must lie in [1, number of competing pooled keys]")
     idx = np.empty((H, n, top_k), dtype=np.int32)
     ranked = np.full((H, n, top_k + 1), -np.inf)
     m = min(top_k + 1, nk)
@@ -297,33 +305,39 @@ def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None):
                 row = s[i]
                 cand = np.nonzero(row >= thr[i])[0]
                 order = sorted(cand.tolist(), key=lambda j: (-row[j], j))
-                idx[h, a + i] = np.sort(np.array(order[:top_k], dtype=np.int32))
+                idx[h, a + i] = first + np.sort(np.array(order[:top_k], dtype=np.int32))
                 ranked[h, a + i, :m] = row[order[:m]]
 
     head_map(one_head, H, workers)
     return idx, ranked
 
 
-def fine_key_rows(geom, block: int, selected: Sequence[int], keep_special: bool = True):
+def fine_key_rows(geom, block: int, selected: Sequence[int], keep_special: bool = True,
+                  keep_ref: bool = False):
     """Token rows attended by the fine branch of one query block: the valid
     tokens of the selected pooled blocks plus, when ``keep_special``, every
     special token of every frame (R5; [Speed3R-it] section 2 keeps the camera
-    tokens, [AVGGT] section 2.2 keeps the special tokens)."""
+    tokens, [AVGGT] section 2.2 keeps the special tokens), plus, when
+    ``keep_ref``, every token of the reference frame 0 (R13)."""
     win = window_table(geom, block)
     parts = [win[j] for j in selected]
+    L = _frame_len(geom)
+    f0 = 1 if keep_ref else 0   # frame 0's special tokens belong to the kept reference frame
+    if keep_ref:
+        parts.append(np.arange(L))
     if keep_special and geom.n_special:
-        L = _frame_len(geom)
-        parts.append(np.concatenate([np.arange(f * L, f * L + geom.n_special)
-                                     for f in range(geom.n_frames)]))
+        parts.append(np.array([f * L + s for f in range(f0, geom.n_frames)
+                               for s in range(geom.n_special)], dtype=np.int64))
     return np.concatenate(parts).astype(np.int64)
 
 
 def fine_attention(q, k, v, geom, block: int, idx, rows=None, keep_special=True,
-                   workers=None):
+                   workers=None, keep_ref=False):
     """Fine-grained attention of each query over only its block's selected
     token blocks ([Speed3R-ja] section 2.1, selection branch, second bullet),
-    plus every special token (R5). ``idx`` [H, N*nqb, K] holds the selected
-    pooled-block indices of every query block."""
+    plus every special token (R5) and, with ``keep_ref``, the whole reference
+    frame (R13). ``idx`` [H, N*nqb, K] holds the selected pooled-block indices
+    of every query block (with ``keep_ref`` none of them in frame 0)."""
     T, H, d = k.shape
     rows = _rows(rows, T)
     qbt = query_block_table(geom, block)
@@ -333,9 +347,11 @@ def fine_attention(q, k, v, geom, block: int, idx, rows=None, keep_special=True,
         owner[members] = b
     blocks = owner[rows]
     L = _frame_len(geom)
-    spec = np.array([f * L + s for f in range(geom.n_frames) for s in range(geom.n_special)],
+    f0 = 1 if keep_ref else 0   # frame 0's special tokens belong to the kept reference frame
+    spec = np.array([f * L + s for f in range(f0, geom.n_frames) for s in range(geom.n_special)],
                     dtype=np.int64)
     use_spec = keep_special and len(spec) > 0
+    ref = np.arange(L if keep_ref else 0)
 
     def one_head(h):
         o = np.empty((len(rows), d))
@@ -347,6 +363,8 @@ def fine_attention(q, k, v, geom, block: int, idx, rows=None, keep_special=True,
             parts = [(k[chosen, h, :], v[chosen, h, :], None)]
             if use_spec:
                 parts.append((ks, vs, None))
+            if keep_ref:
+                parts.append((k[ref, h, :], v[ref, h, :], None))
             o[sel], _ = attend_union(q[rows[sel], h, :], parts)
         return o
 
@@ -366,10 +384,11 @@ def gate(q, o_cmp, o_slc, w, b):
 
 
 def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
-              keep_special=True, workers=None):
+              keep_special=True, workers=None, keep_ref=False):
     """The whole Global Sparse Attention layer for the query rows ``rows``:
     pool, compressed branch, block scores + top-K, fine branch, gate.
-    Returns a dict with every intermediate."""
+    ``keep_ref`` is the VGGT adaptation (R13). Returns a dict with every
+    intermediate."""
     T = q.shape[0]
     rows = _rows(rows, T)
     k_cmp, v_cmp = compress(k, v, geom, block)
@@ -380,12 +399,13 @@ def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
         owner[members] = bi
     need = np.unique(owner[rows])
     q_blk = pooled_queries(q, geom, block, blocks=need)
-    idx_need, ranked = select_topk(q_blk, k_cmp, top_k, workers=workers)
+    first = len(window_table(_one_frame(geom), block)) if keep_ref else 0
+    idx_need, ranked = select_topk(q_blk, k_cmp, top_k, workers=workers, first=first)
     H = q.shape[1]
     idx_full = np.zeros((H, len(qbt), top_k), dtype=np.int32)
     idx_full[:, need] = idx_need
     o_slc = fine_attention(q, k, v, geom, block, idx_full, rows=rows,
-                           keep_special=keep_special, workers=workers)
+                           keep_special=keep_special, workers=workers, keep_ref=keep_ref)
     o = gate(np.asarray(q[rows]), o_cmp, o_slc, w, b)
     return {"k_cmp": k_cmp, "v_cmp": v_cmp, "o_cmp": o_cmp, "blocks": need,
             "q_blk": q_blk, "idx": idx_need, "ranked": ranked, "o_slc": o_slc, "o": o}

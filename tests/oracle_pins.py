@@ -280,6 +280,24 @@ def pin_topk_planted():
         assert idx[0, b].tolist() == want[b], (b, idx[0, b], want[b])
 
 
+def pin_topk_first_brute_force():
+    """With the first F pooled keys left out of the competition (the reference
+    frame's blocks), top-K equals a full sort of the remaining keys' scores, in
+    global indices, for every K."""
+    r = _rng(26)
+    qb = r.standard_normal((6, 2, 8))
+    kc = r.standard_normal((11, 2, 8))
+    s = L.block_scores(qb, kc)
+    F = 4
+    for K in range(1, 8):
+        idx, ranked = L.select_topk(qb, kc, K, first=F)
+        for h in range(2):
+            for b in range(6):
+                want, wr = _brute_topk(list(s[h, b, F:]), K)
+                assert idx[h, b].tolist() == [F + j for j in want], (K, h, b)
+                _close(ranked[h, b, :len(wr)], wr, 1e-13)
+
+
 # ------------------------------------------------------------------- fine
 
 def pin_fine_all_blocks_is_dense():
@@ -303,6 +321,35 @@ def pin_fine_single_corner_token():
     _close(o, np.tile(v[corner], (len(rows), 1, 1)), 1e-15)
 
 
+def _fine_mask(g, idx_h, keep_special=True, keep_ref=False):
+    """Key mask of the fine branch built token by token: query t sees key u
+    when u is a special token (and specials are kept), when u lies in frame 0
+    and the reference frame is kept, or when u's 4x4 window is selected for
+    t's query block. Needs a grid of at most 8 columns (2 windows per row)."""
+    Lf, S = g.tokens_per_frame, g.n_special
+    nbw = -(-g.grid_w // 4)
+    nb = nbw * -(-g.grid_h // 4)
+    nqb = nb + (1 if S else 0)
+    mask = np.zeros((g.n_tokens, g.n_tokens), dtype=bool)
+    for t in range(g.n_tokens):
+        f, p = divmod(t, Lf)
+        if p < S:
+            b = f * nqb + nb
+        else:
+            rr, cc = divmod(p - S, g.grid_w)
+            b = f * nqb + (rr // 4) * nbw + cc // 4
+        for u in range(g.n_tokens):
+            fu, pu = divmod(u, Lf)
+            if keep_ref and fu == 0:
+                mask[t, u] = True
+            elif pu < S:
+                mask[t, u] = keep_special
+            else:
+                ru, cu = divmod(pu - S, g.grid_w)
+                mask[t, u] = fu * nb + (ru // 4) * nbw + cu // 4 in idx_h[b]
+    return mask
+
+
 def pin_fine_vs_masked_sdpa():
     """Fine attention equals SDPA with an explicit per-query key mask built
     token by token from the selected windows and the special tokens."""
@@ -312,26 +359,29 @@ def pin_fine_vs_masked_sdpa():
     nb, nqb = g.n_frames * 4, g.n_frames * 5
     idx = np.stack([np.stack([np.sort(r.choice(nb, 3, replace=False)) for _ in range(nqb)])
                     for _ in range(g.n_heads)]).astype(np.int32)
-    Lf = g.tokens_per_frame
     o = L.fine_attention(q, k, v, g, 4, idx)
     for h in range(g.n_heads):
-        mask = np.zeros((g.n_tokens, g.n_tokens), dtype=bool)
-        for t in range(g.n_tokens):
-            f, p = divmod(t, Lf)
-            if p < g.n_special:
-                b = f * 5 + 4
-            else:
-                rr, cc = divmod(p - g.n_special, g.grid_w)
-                b = f * 5 + (rr // 4) * 2 + cc // 4
-            for u in range(g.n_tokens):
-                fu, pu = divmod(u, Lf)
-                if pu < g.n_special:
-                    mask[t, u] = True
-                    continue
-                ru, cu = divmod(pu - g.n_special, g.grid_w)
-                ju = fu * 4 + (ru // 4) * 2 + cu // 4
-                mask[t, u] = ju in idx[h, b]
-        _close(o[:, h], _sdpa(q[:, h], k[:, h], v[:, h], mask), 1e-12)
+        _close(o[:, h], _sdpa(q[:, h], k[:, h], v[:, h], _fine_mask(g, idx[h])), 1e-12)
+
+
+def pin_ref_frame_vs_masked_sdpa():
+    """The VGGT adaptation: with the reference frame kept, fine attention equals
+    SDPA under the token-by-token mask that adds all of frame 0 to the selected
+    windows (drawn from frames 1..N-1), with and without the special tokens."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 24)
+    r = _rng(25)
+    nqb = g.n_frames * 5
+    idx = np.stack([np.stack([np.sort(r.choice(np.arange(4, g.n_frames * 4), 3, replace=False))
+                              for _ in range(nqb)]) for _ in range(g.n_heads)]).astype(np.int32)
+    for keep_special in (True, False):
+        o = L.fine_attention(q, k, v, g, 4, idx, keep_special=keep_special, keep_ref=True)
+        for h in range(g.n_heads):
+            mask = _fine_mask(g, idx[h], keep_special=keep_special, keep_ref=True)
+            _close(o[:, h], _sdpa(q[:, h], k[:, h], v[:, h], mask), 1e-12)
+    rows = L.fine_key_rows(g, 4, idx[0, 0], keep_special=True, keep_ref=True)
+    want = np.nonzero(_fine_mask(g, idx[0], keep_ref=True)[g.n_special])[0]  # a query of block 0
+    assert sorted(rows.tolist()) == want.tolist()
 
 
 # ------------------------------------------------------------------- gate
@@ -362,6 +412,19 @@ def pin_gsa_forced_fine_all_is_dense():
     w = np.zeros((g.n_heads, 2, g.head_dim))
     b = np.tile([-np.inf, np.inf], (g.n_heads, 1))
     out = L.gsa_layer(q, k, v, g, w, b, top_k=nb)
+    _close(out["o"], L.dense_attention(q, k, v), 1e-12)
+
+
+def pin_gsa_ref_frame_all_is_dense():
+    """The VGGT adaptation with K = every block outside the reference frame and
+    the gate forced to the fine branch is dense attention: every token is
+    attended exactly once, frame 0 through the kept reference frame."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 27)
+    w = np.zeros((g.n_heads, 2, g.head_dim))
+    b = np.tile([-np.inf, np.inf], (g.n_heads, 1))
+    out = L.gsa_layer(q, k, v, g, w, b, top_k=(g.n_frames - 1) * 4, keep_ref=True)
+    assert out["idx"].min() >= 4
     _close(out["o"], L.dense_attention(q, k, v), 1e-12)
 
 

@@ -33,6 +33,14 @@ MUTATIONS = [
      "np.array(order[:top_k], dtype=np.int32)"),
     ("topk_smallest", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (row[j], j)"),
     ("fine_drops_specials", "fine_attention", "if use_spec:", "if False:"),
+    ("ref_specials_twice", "fine_attention", "f0 = 1 if keep_ref else 0", "f0 = 0"),
+    ("ref_frame_dropped", "fine_attention", "            if keep_ref:\n", "            if False:\n"),
+    ("ref_frame_patches_only", "fine_attention", "ref = np.arange(L if keep_ref else 0)",
+     "ref = np.arange(geom.n_special if keep_ref else 0, L if keep_ref else 0)"),
+    ("ref_rows_specials_twice", "fine_key_rows", "f0 = 1 if keep_ref else 0", "f0 = 0"),
+    ("topk_first_ignored", "select_topk", "dtype=np.float64)[first:]", "dtype=np.float64)"),
+    ("topk_first_local_index", "select_topk", "first + np.sort(", "np.sort("),
+    ("gsa_ref_selects_frame0", "gsa_layer", "if keep_ref else 0\n", "if False else 0\n"),
     ("gate_swapped", "gate", "g[..., 0:1] * np.asarray(o_cmp", "g[..., 1:2] * np.asarray(o_cmp"),
     ("gate_no_bias", "gate", " + np.asarray(b, np.float64)", ""),
     ("sga_phase_1", "subsample_plan", "r % s_h == 0 and c % s_w == 0",
