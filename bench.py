@@ -9,6 +9,10 @@ before timing starts):
 Every kernel of the step is launched on torch's current stream; per-call times
 come from HIP events on that stream over the timed region.
 
+After the timed steps, the Speed3R variants of the GSA layer are timed on the
+same inputs, outside the step: the VGGT adaptation (reference frame 0 kept
+whole, top-16 over the other frames) and the test-time top-128.
+
 Prints one JSON line. `value` = tokens of the batch / seconds per step.
 """
 from __future__ import annotations
@@ -37,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=128,
                     help="query rows of the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--variant-steps", type=int, default=1,
+                    help="timed passes of each GSA variant after one untimed pass (0 skips them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) "
                          "so hardware byte counters can be scaled against known traffic")
@@ -88,6 +94,20 @@ def main():
 
     last = {}
 
+    def gsa_chain(ev, i, top_k, keep_ref, ws_f):
+        """The five GSA calls, an event recorded after each."""
+        k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
+        ev[i].record(); i += 1
+        o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
+        ev[i].record(); i += 1
+        idx = sga.gsa_select_topk(q32, k32, geom, top_k, keep_ref=keep_ref)
+        ev[i].record(); i += 1
+        o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, top_k, ws=ws_f, keep_ref=keep_ref)
+        ev[i].record(); i += 1
+        sga.gsa_gate(q, o_cmp, o_slc, w, b, geom)
+        ev[i].record(); i += 1
+        return i, idx
+
     def step(ev):
         i = 0
         ev[i].record(); i += 1
@@ -95,17 +115,7 @@ def main():
         ev[i].record(); i += 1
         sga.dense_global_attn(q, k, v, geom, frame_local=True)
         ev[i].record(); i += 1
-        k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
-        ev[i].record(); i += 1
-        o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
-        ev[i].record(); i += 1
-        idx = sga.gsa_select_topk(q32, k32, geom, wl.top_k)
-        last["idx"] = idx
-        ev[i].record(); i += 1
-        o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, wl.top_k, ws=ws_fine)
-        ev[i].record(); i += 1
-        sga.gsa_gate(q, o_cmp, o_slc, w, b, geom)
-        ev[i].record(); i += 1
+        i, last["idx"] = gsa_chain(ev, i, wl.top_k, False, ws_fine)
         sga.subsampled_global_attn(q, k, v, geom, sh, sw, ws=ws)
         ev[i].record(); i += 1
 
@@ -143,7 +153,7 @@ def main():
     keys_sga = geom.tokens_per_frame + (N - 1) * (mk + has_mean)
     flop_sga = 4.0 * T * keys_sga * d * H
     t_gsa = sum(per[n] for n in names if n.startswith("gsa_"))
-    gsa_roof = gsa_rooflines(geom, wl, per, last["idx"])
+    gsa_roof = gsa_rooflines(geom, per, last["idx"])
     layers = {
         "dense": {"ms": per["dense"], "tokens_per_s": T / per["dense"] * 1e3,
                   "tflops": flop_dense / per["dense"] / 1e9,
@@ -162,6 +172,30 @@ def main():
                        "tflops": flop_sga / per["sga"] / 1e9,
                        "mfma_frac": flop_sga / per["sga"] / 1e9 / PEAK_BF16_TFLOPS},
     }
+    if args.variant_steps > 0:
+        layers["gsa_variants"] = {}
+        for vname, vk, vref in (("vggt_reference_frame", wl.top_k, True), ("top128", 128, False)):
+            ws_v = torch.empty(sga.fine_workspace_bytes(geom, sga.SGA_BF16, True, vref),
+                               dtype=torch.uint8, device=dev)
+            gnames = [n for n in names if n.startswith("gsa_")]
+            vper = {n: 0.0 for n in gnames}
+            for rep in range(1 + args.variant_steps):  # the first pass is untimed
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(gnames) + 1)]
+                ev[0].record()
+                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v)
+                torch.cuda.synchronize()
+                if rep:
+                    for j, n in enumerate(gnames):
+                        vper[n] += ev[j].elapsed_time(ev[j + 1]) / args.variant_steps
+            t_v = sum(vper.values())
+            layers["gsa_variants"][vname] = {
+                "top_k": vk, "reference_frame_kept": vref, "ms": t_v,
+                "tokens_per_s": T / t_v * 1e3, "speedup_vs_dense": per["dense"] / t_v,
+                "kernels_ms": {n[4:]: vper[n] for n in gnames},
+                "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref)}
+            del ws_v, vidx
+            print(f"[bench] variant {vname}: {t_v:.1f} ms", file=sys.stderr, flush=True)
+
     achieved = flop_dense / (per["dense"] * 1e-3) / 1e12
     roofline = {"kernel": "flash_bf16_kernel<GLOBAL> (dense global attention)",
                 "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
@@ -192,12 +226,10 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-PEAK_HBM_GBS = 8000.0
-
-
-def gsa_rooflines(geom, wl, per, idx):
+def gsa_rooflines(geom, per, idx, keep_ref=False):
     """Per-step roofline of the GSA kernels from their timed durations:
-    algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call."""
+    algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call. With
+    ``keep_ref`` frame 0 is attended whole and its blocks do not compete."""
     import torch
     T, H, d, N, S = geom.n_tokens, geom.n_heads, geom.head_dim, geom.n_frames, geom.n_special
     nbh, nbw = -(-geom.grid_h // 4), -(-geom.grid_w // 4)
@@ -210,12 +242,14 @@ def gsa_rooflines(geom, wl, per, idx):
     qcount = torch.cat([win, torch.tensor([S], device=idx.device)])[:nqb] if S else win
     sel = win[(idx.long() % nb)].sum(dim=2)                   # [H, N*nqb] keys chosen
     per_block = qcount.repeat(N)[None, :].double()            # queries per block
-    pairs = float((per_block * (sel.double() + N * S)).sum())  # (query, key) pairs, all heads
+    kept = (geom.tokens_per_frame + (N - 1) * S) if keep_ref else N * S
+    pairs = float((per_block * (sel.double() + kept)).sum())  # (query, key) pairs, all heads
+    n_cand = (N - 1) * nb if keep_ref else N * nb
     out = {}
     pool_bytes = 3 * T * H * d * 2 + N * nb * H * d * (2 + 2 + 4) + N * nqb * H * d * 4
     gate_bytes = 4 * T * H * d * 2
     flops = {"compressed": 4.0 * T * N * nb * d * H,
-             "topk": 3 * 2.0 * d * (N * nqb) * (N * nb) * H,  # three bf16 products per score
+             "topk": 3 * 2.0 * d * (N * nqb) * n_cand * H,  # three bf16 products per score
              "fine": 4.0 * d * pairs}
     for name, nbytes in (("pool", pool_bytes), ("gate", gate_bytes)):
         gbs = nbytes / (per["gsa_" + name] * 1e-3) / 1e9

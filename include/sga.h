@@ -93,37 +93,54 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q,
                         float* k_cmp_f32, float* q_blk_f32, void* stream);
 
 /*
+ * What the GSA selection branch always keeps (gsa_select_topk, gsa_sparse_attn):
+ * SGA_KEEP_SPECIAL: every special token of every frame (the camera tokens the
+ *   Speed3R VGGT adaptation keeps, Italian summary section 2; the special
+ *   tokens kept in AVGGT section 2.2).
+ * SGA_KEEP_REF_FRAME: every token of frame 0, VGGT's reference frame (Speed3R
+ *   technical summary section 2.2, architecture adaptation: the selection
+ *   branch always keeps the reference frame's information). Its pooled blocks
+ *   then take no part in the top-K, which competes among the blocks of frames
+ *   1..N-1 only, so no token is counted twice. Needs N >= 2.
+ */
+enum { SGA_KEEP_SPECIAL = 1, SGA_KEEP_REF_FRAME = 2 };
+
+/*
  * GSA block selection (Speed3R section 2.1, selection branch; the Italian
  * summary's S_guide score matrix): per head h and query block b the score of
  * pooled key j is q_blk[b,h] . k_cmp[j,h] / sqrt(d) (the mean over the block's
  * tokens of their compressed logits); the top_k best j are kept, ties going to
  * the lower j. The score matrix is never materialised.
- * idx:   [H, N*nqb, top_k] int32, each row sorted ascending.
+ * keep: SGA_KEEP_* flags; with SGA_KEEP_REF_FRAME only j >= nb compete.
+ * idx:   [H, N*nqb, top_k] int32 global pooled-key indices, each row ascending.
  * score (nullable): [H, N*nqb, top_k] fp32, the score of each idx entry.
- * 1 <= top_k <= min(N*nb, 128).
+ * 1 <= top_k <= min(competing keys, 128); competing keys = N*nb, or (N-1)*nb
+ * with SGA_KEEP_REF_FRAME.
  */
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
-                           const float* k_cmp_f32, int32_t top_k, int32_t* idx,
-                           float* score, void* stream);
+                           const float* k_cmp_f32, int32_t top_k, int32_t keep,
+                           int32_t* idx, float* score, void* stream);
 
 /*
  * GSA fine attention (Speed3R section 2.1, selection branch): each query of
  * query block b attends to the in-grid tokens of the pooled blocks listed in
- * idx[h, b, :] and, when keep_special == 1, to every special token of every
- * frame (the camera tokens kept by the VGGT adaptation in the Italian summary;
- * special tokens kept in AVGGT section 2.2). One softmax over the union.
- * idx: [H, N*nqb, top_k] int32 entries in [0, N*nb), distinct within a row.
+ * idx[h, b, :] plus what `keep` (SGA_KEEP_* flags) always keeps: every special
+ * token of every frame and/or every token of the reference frame 0. One
+ * softmax over the union.
+ * idx: [H, N*nqb, top_k] int32 entries in [0, N*nb) (in [nb, N*nb) with
+ *   SGA_KEEP_REF_FRAME), distinct within a row; an entry outside that range
+ *   contributes nothing.
  * o_slc: [T, H, d]. lse (nullable): [T, H] fp32.
- * ws: sga_workspace_size(geom, SGA_OP_FINE, keep_special, 0, &bytes) bytes.
- *   bf16 with keep_special == 1 and n_special > 0: the special tokens' keys and
- *   values gathered contiguously, the log-sum-exp of every query over them,
- *   and the dense kernel's staging for them (the special part runs through the
- *   dense attention kernel, the selected windows then continue its softmax).
- *   Otherwise 0 bytes and ws may be NULL.
+ * ws: sga_workspace_size(geom, SGA_OP_FINE, keep, 0, &bytes) bytes. bf16 with
+ *   a non-empty kept set: the kept tokens' keys and values gathered
+ *   contiguously, the log-sum-exp of every query over them, and the dense
+ *   kernel's staging for them (the kept part runs through the dense attention
+ *   kernel, the selected windows then continue its softmax). Otherwise 0
+ *   bytes and ws may be NULL.
  */
 sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q,
                            const void* k, const void* v, const int32_t* idx,
-                           int32_t top_k, int32_t keep_special, void* o_slc,
+                           int32_t top_k, int32_t keep, void* o_slc,
                            float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -168,8 +185,8 @@ enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3 };
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
- * stride_h, stride_w (covers both modes). SGA_OP_FINE: param0 = keep_special,
- * param1 unused (0). */
+ * stride_h, stride_w (covers both modes). SGA_OP_FINE: param0 = keep (the
+ * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

@@ -41,7 +41,7 @@ R11 one mean key/value per *other* frame, the plain mean of that frame's
     dropped patches, entering the softmax as one ordinary key (optionally with
     log(#dropped) added to its logit); omitted when nothing is dropped;
 R12 token order inside a frame: special tokens first, then patches row-major;
-R13 the VGGT adaptation of the selection branch ([Speed3R-ja] section 2.2,
+R15 the VGGT adaptation of the selection branch ([Speed3R-ja] section 2.2,
     architecture adaptation; [Speed3R-it] section 2) keeps the reference frame
     -- frame 0, whose camera fixes VGGT's world coordinates -- whole: every
     query's fine branch attends to all tokens of frame 0, and the top-K is
@@ -282,7 +282,7 @@ def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None, first: 
     section 2, "Ramo di Selezione"). Order: larger score first, ties to the
     lower block index (R6). Returns (idx [H, n, K] int32 ascending,
     ranked [H, n, K+1] fp64 = the K+1 best scores in rank order, +-inf padded).
-    Only pooled keys j >= ``first`` compete (R13: ``first`` = the reference
+    Only pooled keys j >= ``first`` compete (R15: ``first`` = the reference
     frame's block count); the returned indices are global.
     """
     qb = np.asarray(q_blk, dtype=np.float64)
@@ -318,7 +318,7 @@ def fine_key_rows(geom, block: int, selected: Sequence[int], keep_special: bool 
     tokens of the selected pooled blocks plus, when ``keep_special``, every
     special token of every frame (R5; [Speed3R-it] section 2 keeps the camera
     tokens, [AVGGT] section 2.2 keeps the special tokens), plus, when
-    ``keep_ref``, every token of the reference frame 0 (R13)."""
+    ``keep_ref``, every token of the reference frame 0 (R15)."""
     win = window_table(geom, block)
     parts = [win[j] for j in selected]
     L = _frame_len(geom)
@@ -336,7 +336,7 @@ def fine_attention(q, k, v, geom, block: int, idx, rows=None, keep_special=True,
     """Fine-grained attention of each query over only its block's selected
     token blocks ([Speed3R-ja] section 2.1, selection branch, second bullet),
     plus every special token (R5) and, with ``keep_ref``, the whole reference
-    frame (R13). ``idx`` [H, N*nqb, K] holds the selected pooled-block indices
+    frame (R15). ``idx`` [H, N*nqb, K] holds the selected pooled-block indices
     of every query block (with ``keep_ref`` none of them in frame 0)."""
     T, H, d = k.shape
     rows = _rows(rows, T)
@@ -387,7 +387,7 @@ def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
               keep_special=True, workers=None, keep_ref=False):
     """The whole Global Sparse Attention layer for the query rows ``rows``:
     pool, compressed branch, block scores + top-K, fine branch, gate.
-    ``keep_ref`` is the VGGT adaptation (R13). Returns a dict with every
+    ``keep_ref`` is the VGGT adaptation (R15). Returns a dict with every
     intermediate."""
     T = q.shape[0]
     rows = _rows(rows, T)

@@ -21,6 +21,8 @@ SGA_BF16, SGA_F32 = 0, 1
 SGA_OP_SUBSAMPLED = 1
 SGA_OP_DENSE = 2
 SGA_OP_FINE = 3
+SGA_KEEP_SPECIAL = 1
+SGA_KEEP_REF_FRAME = 2
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_select_topk", "gsa_sparse_attn", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
@@ -47,7 +49,7 @@ def library() -> ctypes.CDLL:
     sig = {
         "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
         "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
-        "gsa_select_topk": [G, I32, P, P, I32, P, P, P],
+        "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
         "sga_compact": [G, I32, I32, P, P, P, P, P],
@@ -173,9 +175,15 @@ def gsa_compress(q, k, v, geom, block: int = 4, want_f32: bool = True):
     return k_cmp, v_cmp, k32, q32
 
 
+def keep_flags(keep_special: bool = True, keep_ref: bool = False) -> int:
+    """The SGA_KEEP_* flags: the special tokens and/or the reference frame 0."""
+    return (SGA_KEEP_SPECIAL if keep_special else 0) | (SGA_KEEP_REF_FRAME if keep_ref else 0)
+
+
 def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
-                    want_score: bool = False, dtype_code: int = SGA_BF16):
-    """Top-K pooled blocks per (head, query block), ascending; see include/sga.h."""
+                    want_score: bool = False, dtype_code: int = SGA_BF16, keep_ref: bool = False):
+    """Top-K pooled blocks per (head, query block), ascending; with ``keep_ref``
+    frame 0's blocks do not compete (it is kept whole); see include/sga.h."""
     H, d, N = geom.n_heads, 64, geom.n_frames
     nb, nqb = pooled_shape(geom, block)
     _need(q_blk_f32, "q_blk_f32", N * nqb, H, d, torch.float32)
@@ -185,22 +193,26 @@ def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
                         device=q_blk_f32.device) if want_score else None
     g = make_geom(geom, dtype_code)
     _check(library().gsa_select_topk(ctypes.byref(g), block, _ptr(q_blk_f32), _ptr(k_cmp_f32),
-                                     top_k, _ptr(idx), _ptr(score), _stream(q_blk_f32)),
+                                     top_k, keep_flags(False, keep_ref), _ptr(idx), _ptr(score),
+                                     _stream(q_blk_f32)),
            "gsa_select_topk")
     return (idx, score) if want_score else idx
 
 
-def fine_workspace_bytes(geom, dtype_code: int, keep_special: bool = True) -> int:
+def fine_workspace_bytes(geom, dtype_code: int, keep_special: bool = True,
+                         keep_ref: bool = False) -> int:
     n = ctypes.c_size_t(0)
     g = make_geom(geom, dtype_code)
-    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_FINE, int(keep_special), 0,
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_FINE,
+                                        keep_flags(keep_special, keep_ref), 0,
                                         ctypes.byref(n)), "sga_workspace_size")
     return n.value
 
 
 def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, block: int = 4,
-                    want_lse: bool = False, ws=None):
-    """Fine attention over the selected blocks (+ all special tokens); see include/sga.h."""
+                    want_lse: bool = False, ws=None, keep_ref: bool = False):
+    """Fine attention over the selected blocks (+ all special tokens, + frame 0
+    whole with ``keep_ref``); see include/sga.h."""
     T, H, d, N = tokens(geom), geom.n_heads, 64, geom.n_frames
     nb, nqb = pooled_shape(geom, block)
     _need(q, "q", T, H, d)
@@ -212,9 +224,10 @@ def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, b
     lse = torch.empty((T, H), dtype=torch.float32, device=q.device) if want_lse else None
     code = _dtype_code(q)
     g = make_geom(geom, code)
-    ws = _workspace(fine_workspace_bytes(geom, code, keep_special), q.device, ws)
+    ws = _workspace(fine_workspace_bytes(geom, code, keep_special, keep_ref), q.device, ws)
     _check(library().gsa_sparse_attn(ctypes.byref(g), block, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                     top_k, int(keep_special), _ptr(o), _ptr(lse), _ptr(ws),
+                                     top_k, keep_flags(keep_special, keep_ref), _ptr(o), _ptr(lse),
+                                     _ptr(ws),
                                      0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(q)),
            "gsa_sparse_attn")
@@ -288,15 +301,16 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 
 
 def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
-              keep_special: bool = True, keep_intermediates: bool = False):
+              keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False):
     """The Global Sparse Attention layer as its five library calls, in order:
-    compress, compressed attention, select, fine attention, gate."""
+    compress, compressed attention, select, fine attention, gate. ``keep_ref``
+    is the VGGT adaptation: frame 0 kept whole by the fine branch."""
     N = geom.n_frames
     nb, _ = pooled_shape(geom, block)
     k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block)
     o_cmp = dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
-    idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q))
-    o_slc = gsa_sparse_attn(q, k, v, idx, geom, top_k, keep_special, block)
+    idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q), keep_ref=keep_ref)
+    o_slc = gsa_sparse_attn(q, k, v, idx, geom, top_k, keep_special, block, keep_ref=keep_ref)
     o = gsa_gate(q, o_cmp, o_slc, w_gate, b_gate, geom)
     if keep_intermediates:
         return {"k_cmp": k_cmp, "v_cmp": v_cmp, "k_cmp_f32": k32, "q_blk_f32": q32,

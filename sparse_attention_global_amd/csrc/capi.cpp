@@ -11,6 +11,9 @@
 #include "../../include/sga.h"
 #include "kernels.hpp"
 
+static_assert(SGA_KEEP_SPECIAL == sga::kKeepSpecial && SGA_KEEP_REF_FRAME == sga::kKeepRefFrame,
+              "keep flags of the C ABI and the kernels agree");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -81,10 +84,24 @@ sga_status check_block(int32_t block) {
   return SGA_OK;
 }
 
-sga_status check_topk(const sga::Geom& g, int32_t top_k) {
-  const long long n_cand = (long long)g.n_frames * g.nb;
+sga_status check_keep(const sga::Geom& g, int32_t keep) {
+  if (keep < 0 || keep > (SGA_KEEP_SPECIAL | SGA_KEEP_REF_FRAME))
+    return fail(SGA_ERR_INVALID_ARG, "keep %d must be a combination of SGA_KEEP_SPECIAL and SGA_KEEP_REF_FRAME", keep);
+  if ((keep & SGA_KEEP_REF_FRAME) && g.n_frames < 2)
+    return fail(SGA_ERR_INVALID_ARG, "SGA_KEEP_REF_FRAME needs at least 2 frames");
+  return SGA_OK;
+}
+
+// First pooled key that competes in the top-K: the reference frame's blocks
+// are kept whole, so they do not compete.
+int first_candidate(const sga::Geom& g, int32_t keep) { return (keep & SGA_KEEP_REF_FRAME) ? g.nb : 0; }
+
+sga_status check_topk(const sga::Geom& g, int32_t top_k, int32_t keep) {
+  if (sga_status st = check_keep(g, keep)) return st;
+  const long long n_cand = (long long)g.n_frames * g.nb - first_candidate(g, keep);
   if (top_k < 1 || top_k > n_cand || top_k > 128)
-    return fail(SGA_ERR_INVALID_ARG, "top_k %d must lie in [1, min(N*nb = %lld, 128)]", top_k, n_cand);
+    return fail(SGA_ERR_INVALID_ARG, "top_k %d must lie in [1, min(competing blocks = %lld, 128)]", top_k,
+                n_cand);
   return SGA_OK;
 }
 
@@ -104,8 +121,10 @@ sga_status check_fits(const sga::FlashLaunch& p) {
   return SGA_OK;
 }
 
-// gsa_sparse_attn workspace (bf16 with specials): gathered K and V of the
-// N*S special tokens, the queries' log-sum-exp over them, the dense staging.
+// gsa_sparse_attn workspace (bf16 with a non-empty kept set): gathered K and V
+// of the kept tokens (frame 0 whole when the reference frame is kept, then the
+// special tokens of the remaining frames), the queries' log-sum-exp over them,
+// the dense staging.
 struct FineLayout {
   long long rows = 0;
   size_t kv = 0, lse = 0, flash = 0, total = 0;
@@ -121,10 +140,10 @@ sga::FlashLaunch dense_launch(const sga::Geom& g, int64_t n_keys, int32_t frame_
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-FineLayout fine_layout(const sga::Geom& g, bool bf, int keep_special) {
+FineLayout fine_layout(const sga::Geom& g, bool bf, int keep) {
   FineLayout lay;
-  lay.rows = (long long)g.n_frames * g.n_special;
-  if (!bf || !keep_special || lay.rows == 0) return lay;
+  lay.rows = sga::kept_rows(g, keep);
+  if (!bf || lay.rows == 0) return lay;
   lay.kv = round256((size_t)lay.rows * g.n_heads * sga::kHeadDim * 2);
   lay.lse = round256((size_t)g.T * g.n_heads * sizeof(float));
   lay.flash = round256(sga::flash_bf16_workspace(dense_launch(g, lay.rows, 0)));
@@ -205,55 +224,52 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, cons
 }
 
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
-                           const float* k_cmp_f32, int32_t top_k, int32_t* idx, float* score,
-                           void* stream) {
+                           const float* k_cmp_f32, int32_t top_k, int32_t keep, int32_t* idx,
+                           float* score, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
-  if (sga_status st = check_topk(g, top_k)) return st;
+  if (sga_status st = check_topk(g, top_k, keep)) return st;
   REQUIRE_PTR(q_blk_f32);
   REQUIRE_PTR(k_cmp_f32);
   REQUIRE_PTR(idx);
   REQUIRE_OPT_PTR(score);
-  return from_hip(sga::launch_gsa_topk(g, q_blk_f32, k_cmp_f32, top_k, idx, score,
-                                       static_cast<hipStream_t>(stream)),
+  return from_hip(sga::launch_gsa_topk(g, q_blk_f32, k_cmp_f32, top_k, first_candidate(g, keep), idx,
+                                       score, static_cast<hipStream_t>(stream)),
                   "gsa_select_topk launch");
 }
 
 sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
-                           const void* v, const int32_t* idx, int32_t top_k, int32_t keep_special,
+                           const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
                            void* o_slc, float* lse, void* ws, size_t ws_bytes, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
-  if (sga_status st = check_topk(g, top_k)) return st;
+  if (sga_status st = check_topk(g, top_k, keep)) return st;
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(idx);
   REQUIRE_PTR(o_slc);
   REQUIRE_OPT_PTR(lse);
-  if (keep_special != 0 && keep_special != 1) return fail(SGA_ERR_INVALID_ARG, "keep_special must be 0 or 1");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = geom->dtype == SGA_BF16;
-  const FineLayout lay = fine_layout(g, bf, keep_special);
+  const FineLayout lay = fine_layout(g, bf, keep);
   if (lay.total == 0)
-    return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep_special, o_slc, lse,
+    return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, o_slc, lse,
                                          nullptr, nullptr, s),
                     "gsa_sparse_attn launch");
   if (ws == nullptr || ws_bytes < lay.total)
     return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
                 ws == nullptr ? 0 : ws_bytes);
   if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
-  // the special tokens of every frame through the dense kernel: o_slc and the
-  // log-sum-exp hold that partial result, which the window kernel continues
+  // the kept tokens through the dense kernel: o_slc and the log-sum-exp hold
+  // that partial result, which the window kernel continues
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* k_s = w;
   void* v_s = w + lay.kv;
   float* lse_s = reinterpret_cast<float*>(w + 2 * lay.kv);
   void* flash_ws = w + 2 * lay.kv + lay.lse;
-  if (hipError_t e = sga::launch_gather_specials(g, k, v, k_s, v_s, s))
-    return from_hip(e, "gsa_sparse_attn (specials) launch");
   sga::FlashLaunch p = dense_launch(g, lay.rows, 0);
   p.q = q;
   p.k = k_s;
@@ -261,9 +277,11 @@ sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, c
   p.o = o_slc;
   p.lse = lse_s;
   if (sga_status st = check_fits(p)) return st;
+  if (hipError_t e = sga::launch_gather_kept(g, keep, k, v, k_s, v_s, s))
+    return from_hip(e, "gsa_sparse_attn (kept tokens) launch");
   if (hipError_t e = sga::launch_flash_bf16(p, flash_ws, s))
-    return from_hip(e, "gsa_sparse_attn (specials attention) launch");
-  return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, 0, o_slc, lse,
+    return from_hip(e, "gsa_sparse_attn (kept tokens attention) launch");
+  return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, o_slc, lse,
                                        static_cast<const sga::bf16*>(o_slc), lse_s, s),
                   "gsa_sparse_attn launch");
 }
@@ -309,8 +327,8 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
     return SGA_OK;
   }
   if (op == SGA_OP_FINE) {
-    if ((param0 != 0 && param0 != 1) || param1 != 0)
-      return fail(SGA_ERR_INVALID_ARG, "fine workspace: param0 = keep_special (0/1), param1 = 0");
+    if (param1 != 0) return fail(SGA_ERR_INVALID_ARG, "fine workspace: param1 must be 0");
+    if (sga_status st = check_keep(g, param0)) return st;
     *bytes = fine_layout(g, geom->dtype == SGA_BF16, param0).total;
     return SGA_OK;
   }
@@ -382,6 +400,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 20000; }
+int32_t sga_version(void) { return 30000; }
 
 }  // extern "C"

@@ -1,11 +1,13 @@
 // GSA fine attention (Speed3R technical summary section 2.1, selection branch):
 // every query of query block b attends to the in-grid tokens of the pooled
-// blocks selected for b and, when asked, to every special token of every frame
-// (kept whole: the camera tokens of the VGGT adaptation in the Italian summary;
-// the special tokens of AVGGT section 2.2).
+// blocks selected for b and, when asked, to the always-kept tokens: every
+// special token of every frame (the camera tokens of the VGGT adaptation in
+// the Italian summary; the special tokens of AVGGT section 2.2) and every token
+// of the reference frame 0 (the VGGT adaptation, Speed3R technical summary
+// section 2.2).
 //
-// bf16: the special tokens are the same keys for every query, so that part is
-// dense attention over N*S keys: the C ABI gathers them and runs the dense
+// bf16: the kept tokens are the same keys for every query, so that part is
+// dense attention over them: the C ABI gathers them and runs the dense
 // kernel, which leaves every query's normalised partial output and its
 // log-sum-exp. This kernel then starts each query's online softmax from that
 // partial result (as one pre-merged key: logit = its log-sum-exp, value = its
@@ -39,7 +41,7 @@ struct FineArgs {
   const float* lse_init;  // its log-sum-exp (natural log of the scaled logits)
   Geom g;
   int top_k;
-  int keep_special;  // (bf16: 0; the special tokens arrive through o_init)
+  int w_lo;          // first pooled window that may contribute (nb when frame 0 is kept whole)
   int n_wg_per_head;
   float c;
 };
@@ -56,9 +58,9 @@ __device__ __forceinline__ long long block_member_row(const Geom& g, long long b
 }
 
 // Token row of slot p (0..15) of pooled window w, or -1 outside the grid (or
-// for a window index outside [0, N*nb), which therefore selects nothing).
-__device__ __forceinline__ long long window_slot_row(const Geom& g, int w, int p) {
-  if (w < 0 || w >= g.n_frames * g.nb) return -1;
+// for a window index outside [w_lo, N*nb), which therefore selects nothing).
+__device__ __forceinline__ long long window_slot_row(const Geom& g, int w_lo, int w, int p) {
+  if (w < w_lo || w >= g.n_frames * g.nb) return -1;
   const int f = w / g.nb, j = w % g.nb;
   const int r = 4 * (j / g.nbw) + (p >> 2), c = 4 * (j % g.nbw) + (p & 3);
   if (r >= g.grid_h || c >= g.grid_w) return -1;
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
         for (int i = 0; i < 2; ++i) {
           const int wi = 4 * t + ((u + i) >> 4);
           long long row = -1;
-          if (bvalid && wi < A.top_k) row = window_slot_row(g, sel[wi], (u + i) & 15);
+          if (bvalid && wi < A.top_k) row = window_slot_row(g, A.w_lo, sel[wi], (u + i) & 15);
           rows[i] = row;
           if (row >= 0) {
             kreg[i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
@@ -138,12 +140,12 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
 }
 
 // fp32 path: one thread per (query, head), exact online softmax over the same
-// key set (special tokens, then the selected windows' in-grid tokens).
+// key set (the kept tokens, then the selected windows' in-grid tokens).
 __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* __restrict__ q,
                                                           const float* __restrict__ k,
                                                           const float* __restrict__ v,
                                                           const int32_t* __restrict__ idx,
-                                                          int top_k, int keep_special,
+                                                          int top_k, int keep,
                                                           float* __restrict__ o,
                                                           float* __restrict__ lse) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -175,14 +177,17 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
     l = l * alpha + pe;
     m = m_new;
   };
-  if (keep_special)
-    for (int ff = 0; ff < g.n_frames; ++ff)
+  const bool ref = (keep & kKeepRefFrame) != 0;
+  if (ref)
+    for (long long row = 0; row < g.L; ++row) visit(row);
+  if (keep & kKeepSpecial)
+    for (int ff = ref ? 1 : 0; ff < g.n_frames; ++ff)
       for (int s = 0; s < g.n_special; ++s) visit((long long)ff * g.L + s);
   const long long n_qb = (long long)g.n_frames * g.nqb;
   const int32_t* sel = idx + ((long long)h * n_qb + b) * top_k;
   for (int i = 0; i < top_k; ++i)
     for (int slot = 0; slot < 16; ++slot) {
-      const long long row = window_slot_row(g, sel[i], slot);
+      const long long row = window_slot_row(g, ref ? g.nb : 0, sel[i], slot);
       if (row >= 0) visit(row);
     }
   float* op = o + t * rs + hoff;
@@ -190,50 +195,56 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
   if (lse) lse[t * g.n_heads + h] = m + logf(l);
 }
 
-// k_s[u] = k[row of special token u] (u = f * S + s), likewise v: a thread per
-// 16-byte chunk.
-__global__ __launch_bounds__(256) void gather_specials_kernel(Geom g, const u32x4* __restrict__ k,
-                                                              const u32x4* __restrict__ v,
-                                                              u32x4* __restrict__ k_s,
-                                                              u32x4* __restrict__ v_s) {
+// k_s[u] = k[row of kept token u], likewise v, in kept_rows order: frame 0's
+// L tokens when it is kept whole, then the special tokens (u' = f' * S + s) of
+// the frames after it. A thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void gather_kept_kernel(Geom g, long long n_ref, int f0, long long n,
+                                                          const u32x4* __restrict__ k,
+                                                          const u32x4* __restrict__ v,
+                                                          u32x4* __restrict__ k_s,
+                                                          u32x4* __restrict__ v_s) {
   const long long chunks_per_row = (long long)g.n_heads * kHeadDim / 8;
-  const long long n = (long long)g.n_frames * g.n_special * chunks_per_row;
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const long long u = i / chunks_per_row, ch = i % chunks_per_row;
-  const long long row = (u / g.n_special) * g.L + (u % g.n_special);
+  long long row = u;
+  if (u >= n_ref) {
+    const long long us = u - n_ref;
+    row = (f0 + us / g.n_special) * g.L + us % g.n_special;
+  }
   k_s[i] = k[row * chunks_per_row + ch];
   v_s[i] = v[row * chunks_per_row + ch];
 }
 
 }  // namespace
 
-hipError_t launch_gather_specials(const Geom& g, const void* k, const void* v, void* k_s,
-                                  void* v_s, hipStream_t stream) {
-  const long long n = (long long)g.n_frames * g.n_special * g.n_heads * kHeadDim / 8;
+hipError_t launch_gather_kept(const Geom& g, int keep, const void* k, const void* v, void* k_s,
+                              void* v_s, hipStream_t stream) {
+  const bool ref = (keep & kKeepRefFrame) != 0;
+  const long long n = kept_rows(g, keep) * g.n_heads * kHeadDim / 8;
   const long long blocks = (n + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_specials_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g,
-                     static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
-                     static_cast<u32x4*>(k_s), static_cast<u32x4*>(v_s));
+  hipLaunchKernelGGL(gather_kept_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g,
+                     ref ? (long long)g.L : 0LL, ref ? 1 : 0, n, static_cast<const u32x4*>(k),
+                     static_cast<const u32x4*>(v), static_cast<u32x4*>(k_s), static_cast<u32x4*>(v_s));
   return hipGetLastError();
 }
 
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
-                           const void* v, const int32_t* idx, int top_k, int keep_special,
+                           const void* v, const int32_t* idx, int top_k, int keep,
                            void* o, float* lse, const bf16* o_init, const float* lse_init,
                            hipStream_t stream) {
   if (!is_bf16) {
     dim3 grid((unsigned)((g.T + 63) / 64), (unsigned)g.n_heads);
     hipLaunchKernelGGL(gsa_fine_f32_kernel, grid, dim3(64), 0, stream, g,
                        static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), idx, top_k, keep_special,
+                       static_cast<const float*>(v), idx, top_k, keep,
                        static_cast<float*>(o), lse);
     return hipGetLastError();
   }
-  // bf16: the special tokens come in through o_init / lse_init only
-  if (keep_special && g.n_special > 0) return hipErrorInvalidValue;
+  // bf16: the kept tokens come in through o_init / lse_init only
+  if (kept_rows(g, keep) > 0 && (o_init == nullptr || lse_init == nullptr)) return hipErrorInvalidValue;
   FineArgs A{};
   A.q = static_cast<const bf16*>(q);
   A.k = static_cast<const bf16*>(k);
@@ -243,7 +254,7 @@ hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const voi
   A.lse = lse;
   A.g = g;
   A.top_k = top_k;
-  A.keep_special = keep_special;
+  A.w_lo = (keep & kKeepRefFrame) ? g.nb : 0;
   A.o_init = o_init;
   A.lse_init = lse_init;
   A.c = kLog2e / sqrtf((float)kHeadDim);

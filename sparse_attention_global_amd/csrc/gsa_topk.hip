@@ -4,8 +4,10 @@
 // matrix).
 //
 // Per head h and query block b, score(j) = q_blk[b,h] . k_cmp[j,h] / sqrt(d)
-// for every pooled key j; the top_k best (larger score first, ties to the lower
-// j) are returned as an ascending index set.
+// for every competing pooled key j; the top_k best (larger score first, ties
+// to the lower j) are returned as an ascending index set. The competing keys
+// are all pooled keys, or those after the reference frame's blocks when that
+// frame is kept whole (Speed3R technical summary section 2.2, VGGT adaptation).
 //
 // Scores: fp32-accurate products on the bf16 matrix cores via the three-term
 // split x = hi + lo (hi = bf16(x), lo = bf16(x - hi)):
@@ -48,6 +50,7 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 
 __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __restrict__ q_blk,
                                                        const float* __restrict__ k_cmp,
+                                                       long long n_cand, int j0,
                                                        int top_k, int n_rowtiles,
                                                        int32_t* __restrict__ idx,
                                                        float* __restrict__ score) {
@@ -56,7 +59,6 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
   const int h = blockIdx.x / n_rowtiles;
   const long long row0 = (long long)(blockIdx.x % n_rowtiles) * 32 * waves;
   const long long n_rows = (long long)g.n_frames * g.nqb;
-  const long long n_cand = (long long)g.n_frames * g.nb;
   const long long rs = (long long)g.n_heads * kHeadDim;
   const long long hoff = (long long)h * kHeadDim;
 
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
         const int jj = my_j[p];
         if (jj > prev && jj < best) { best = jj; bp = p; }
       }
-      ip[o] = best;
+      ip[o] = best + j0;
       if (sp) sp[o] = my_v[bp];
       prev = best;
     }
@@ -252,6 +254,7 @@ __device__ __forceinline__ bool better(float s, int j, float ts, int tj) {
 template <bool FULL>  // FULL: top_k == kRegK, the threshold is the list's last slot
 __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const float* __restrict__ q_blk,
                                                            const float* __restrict__ k_cmp,
+                                                           long long n_cand, int j0,
                                                            int top_k, int n_rowtiles,
                                                            int32_t* __restrict__ idx,
                                                            float* __restrict__ score) {
@@ -259,7 +262,6 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   const int h = blockIdx.x / n_rowtiles;
   const long long row0 = (long long)(blockIdx.x % n_rowtiles) * 128;
   const long long n_rows = (long long)g.n_frames * g.nqb;
-  const long long n_cand = (long long)g.n_frames * g.nb;
   const long long rs = (long long)g.n_heads * kHeadDim;
   const long long hoff = (long long)h * kHeadDim;
 
@@ -456,7 +458,7 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
         best = in ? lj[p] : best;
         bv = in ? lv[p] : bv;
       }
-      ip[o] = best;
+      ip[o] = best + j0;
       if (sp) sp[o] = bv;
       prev = best;
     }
@@ -466,18 +468,22 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
 }  // namespace
 
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
-                           int32_t* idx, float* score, hipStream_t stream) {
+                           int first, int32_t* idx, float* score, hipStream_t stream) {
   const long long n_rows = (long long)g.n_frames * g.nqb;
+  // the kernels see the competing keys only, indexed from 0, and add `first`
+  // to the indices they write
+  const long long n_cand = (long long)g.n_frames * g.nb - first;
+  const float* kc = k_cmp + (long long)first * g.n_heads * kHeadDim;
   if (top_k <= kRegK) {
     const int n_rowtiles = (int)((n_rows + 127) / 128);
     const long long grid = (long long)n_rowtiles * g.n_heads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (top_k == kRegK) {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<true>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, k_cmp, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
     } else {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<false>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, k_cmp, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
     }
     return hipGetLastError();
   }
@@ -488,7 +494,7 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
   const long long grid = (long long)n_rowtiles * g.n_heads;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gsa_topk_kernel, dim3((unsigned)grid), dim3(64 * waves), lds_for(waves), stream,
-                     g, q_blk, k_cmp, top_k, n_rowtiles, idx, score);
+                     g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
   return hipGetLastError();
 }
 

@@ -48,22 +48,38 @@ hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const voi
                            const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
                            float* q_blk_f32, hipStream_t stream);
 
-// GSA top-K block selection (gsa_topk.hip).
-hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
-                           int32_t* idx, float* score, hipStream_t stream);
+// What the GSA selection branch always keeps (the values of the C ABI's
+// SGA_KEEP_* flags): every special token; every token of reference frame 0.
+constexpr int kKeepSpecial = 1;
+constexpr int kKeepRefFrame = 2;
 
-// GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32. With o_init/lse_init
-// (bf16 only) every query's softmax starts from that partial result (the
-// attention over the special tokens, normalised, and its log-sum-exp) and the
-// selected windows continue it; keep_special must then be 0.
+// Number of always-kept tokens: frame 0 whole (with kKeepRefFrame), then the
+// special tokens of the remaining frames (with kKeepSpecial).
+inline long long kept_rows(const Geom& g, int keep) {
+  const bool ref = (keep & kKeepRefFrame) != 0;
+  const long long specials = (keep & kKeepSpecial) ? (long long)(g.n_frames - (ref ? 1 : 0)) * g.n_special : 0;
+  return (ref ? (long long)g.L : 0) + specials;
+}
+
+// GSA top-K block selection (gsa_topk.hip). Pooled keys first .. N*nb-1
+// compete; idx holds global indices.
+hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
+                           int first, int32_t* idx, float* score, hipStream_t stream);
+
+// GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32. keep: kKeep* flags.
+// fp32 visits the kept tokens itself. bf16 takes them through o_init/lse_init
+// (required when kept_rows(g, keep) > 0): every query's softmax starts from
+// that partial result (the attention over the kept tokens, normalised, and its
+// log-sum-exp) and the selected windows continue it. With kKeepRefFrame a
+// window of frame 0 in idx contributes nothing (frame 0 is already counted).
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
-                           const void* v, const int32_t* idx, int top_k, int keep_special,
+                           const void* v, const int32_t* idx, int top_k, int keep,
                            void* o, float* lse, const bf16* o_init, const float* lse_init,
                            hipStream_t stream);
-// The N*S special tokens' keys and values, gathered contiguously (frame-major,
-// [N*S, H, d]) for the dense kernel (gsa_fine.hip).
-hipError_t launch_gather_specials(const Geom& g, const void* k, const void* v, void* k_s,
-                                  void* v_s, hipStream_t stream);
+// The kept tokens' keys and values, gathered contiguously ([kept_rows, H, d],
+// in kept_rows order) for the dense kernel (gsa_fine.hip).
+hipError_t launch_gather_kept(const Geom& g, int keep, const void* k, const void* v, void* k_s,
+                              void* v_s, hipStream_t stream);
 
 // GSA gate (gsa_gate.hip).
 hipError_t launch_gsa_gate(const Geom& g, bool is_bf16, const void* q, const void* o_cmp,

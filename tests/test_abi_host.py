@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 20000
+    assert library().sga_version() == 30000
 
 
 def geom(**kw):
@@ -89,11 +89,22 @@ def test_gsa_calls_reject_bad_arguments():
     assert L.gsa_compress(ctypes.byref(g), 4, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
     nb = 2 * 100
     for bad_k in (0, nb + 1, 129):
-        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, FAKE, None, None) == INVALID
+        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, 0, FAKE, None, None) == INVALID
         assert "top_k" in last_error()
-    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 2, FAKE, None, None, 0,
+    # with the reference frame kept whole only the other frame's 100 blocks compete
+    assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 101, 2, FAKE, None, None) == INVALID
+    assert "competing blocks = 100" in last_error()
+    assert L.gsa_select_topk(ctypes.byref(geom(n_frames=1)), 4, FAKE, FAKE, 4, 2, FAKE, None,
                              None) == INVALID
-    assert "keep_special" in last_error()
+    assert "2 frames" in last_error()
+    for bad_keep in (-1, 4):
+        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 16, bad_keep, FAKE, None,
+                                 None) == INVALID
+        assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, bad_keep, FAKE, None,
+                                 None, 0, None) == INVALID
+        assert "keep" in last_error()
+    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 101, 3, FAKE, None, None, 0,
+                             None) == INVALID
     assert L.gsa_gate(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
 
 
@@ -151,23 +162,34 @@ def test_workspace_sizes():
 def test_fine_workspace():
     g = geom(n_frames=256)
     T = 256 * 1374
-    # bf16 with the special tokens: their gathered K and V (256 frames x 5), the
-    # queries' log-sum-exp over them, and the dense staging for 1280 keys
-    # (V^T, key-norm partials, one redo flag per 128-query workgroup)
-    kv = r256(1280 * 16 * 64 * 2)
     lse = r256(T * 16 * 4)
-    flash = r256(16 * 64 * 1280 * 2 + 16 * 256 * 4 + r256(-(-T // 128) * 16))
-    assert _ws(g, 3, 1, 0) == (OK, 2 * kv + lse + flash)
+
+    def expect(rows):
+        # the kept tokens' gathered K and V, the queries' log-sum-exp over them,
+        # and the dense staging for those keys (V^T, key-norm partials, one redo
+        # flag per 128-query workgroup)
+        kv = r256(rows * 16 * 64 * 2)
+        flash = r256(16 * 64 * ((rows + 63) // 64 * 64) * 2 + 16 * 256 * 4 + r256(-(-T // 128) * 16))
+        return 2 * kv + lse + flash
+
+    # special tokens only: 256 frames x 5
+    assert _ws(g, 3, 1, 0) == (OK, expect(1280))
+    # reference frame only: frame 0's 1374 tokens
+    assert _ws(g, 3, 2, 0) == (OK, expect(1374))
+    # both: frame 0 whole, then the 255 other frames' 5 specials
+    assert _ws(g, 3, 3, 0) == (OK, expect(1374 + 255 * 5))
     assert _ws(g, 3, 0, 0) == (OK, 0)
     assert _ws(geom(n_frames=4, n_special=0), 3, 1, 0) == (OK, 0)
-    assert _ws(geom(n_frames=4, dtype=1), 3, 1, 0) == (OK, 0)
-    assert _ws(g, 3, 2, 0)[0] == INVALID
+    assert _ws(geom(n_frames=4, dtype=1), 3, 3, 0) == (OK, 0)
+    assert _ws(g, 3, 4, 0)[0] == INVALID
+    assert _ws(geom(n_frames=1), 3, 2, 0)[0] == INVALID
     assert _ws(g, 3, 1, 7)[0] == INVALID
     # a missing workspace is reported before anything is launched
     L = library()
-    assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, None,
-                             None, 0, None) == WORKSPACE
-    assert "workspace" in last_error()
+    for keep in (1, 2, 3):
+        assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, keep, FAKE, None,
+                                 None, 0, None) == WORKSPACE
+        assert "workspace" in last_error()
 
 
 def test_python_layer_requires_gpu_tensors():

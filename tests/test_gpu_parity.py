@@ -255,6 +255,89 @@ def test_topk_widths(top_k):
         assert np.max(np.abs(s_h[h] - ref)) < 1e-4
 
 
+# ---------------------------------------------------------------------------
+# Speed3R architecture variants: VGGT (reference frame 0 kept whole, the top-K
+# over the other frames) and pi^3 (no register tokens)
+# ---------------------------------------------------------------------------
+
+def _layer_on_decided_rows(geom, q, k, v, w, b, top_k, keep_ref, what):
+    out = sga.gsa_layer(q, k, v, w, b, geom, top_k, keep_ref=keep_ref)
+    _sync()
+    ref = oracle.gsa_layer(host(q), host(k), host(v), geom, host(w), host(b), top_k,
+                           keep_ref=keep_ref)
+    dec = decided_blocks(ref["ranked"], top_k).all(axis=0)
+    owner = _owner_blocks(geom, np.arange(geom.n_tokens))
+    pos = {bb: i for i, bb in enumerate(ref["blocks"])}
+    rows = np.array([t for t in range(geom.n_tokens) if dec[pos[owner[t]]]])
+    # many close block scores (top-32 of 175) leave few blocks decided in every
+    # head; the index sets and the fine branch are checked in full separately
+    print(f"[parity] {what}: {len(rows)} of {geom.n_tokens} rows decided in every head", flush=True)
+    assert len(rows) >= 64
+    assert_close(host(out)[rows], ref["o"][rows], geom.dtype, what)
+
+
+VGGT = [
+    pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), 5, id="ragged-bf16"),
+    pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), 3, id="ragged-f32"),
+    pytest.param(Geometry(8, 5, 20, 20, 2, 64, "bf16"), 16, id="3-tiles-top16"),
+    pytest.param(Geometry(8, 5, 20, 20, 2, 64, "bf16"), 32, id="3-tiles-top32"),
+    pytest.param(Geometry(4, 0, 13, 11, 2, 64, "bf16"), 6, id="no-specials"),
+]
+
+
+@pytest.mark.parametrize("geom,top_k", VGGT)
+def test_reference_frame_kept(geom, top_k):
+    """The VGGT adaptation: selection among frames 1..N-1 only, frame 0 attended
+    whole by every query (with and without the special tokens), and a frame-0
+    window slipped into an index list contributes nothing."""
+    _announce(f"reference frame kept {geom} top_k={top_k}")
+    dist = "normal" if geom.dtype == "f32" else "scene"
+    q, k, v = make_qkv(geom, seed=41, device=DEV, distribution=dist)
+    w, b = make_gate(geom.n_heads, 64, seed=41, device=DEV)
+    qh, kh, vh = host(q), host(k), host(v)
+    nb = _nb(geom)
+    _, _, k32, q32 = sga.gsa_compress(q, k, v, geom)
+    idx, score = sga.gsa_select_topk(q32, k32, geom, top_k, want_score=True, keep_ref=True)
+    _sync()
+    rkc, _ = oracle.compress(kh, vh, geom, 4)
+    rqb = oracle.pooled_queries(qh, geom, 4)
+    ridx, ranked = oracle.select_topk(rqb, rkc, top_k, first=nb)
+    idx_h = host(idx).astype(np.int64)
+    assert idx_h.min() >= nb
+    check_topk(idx_h, ridx, ranked, rqb, rkc, "top-K (reference frame kept)")
+    for h in range(geom.n_heads):
+        s = np.einsum("bkd,bd->bk", rkc[idx_h[h], h, :], rqb[:, h, :]) / 8.0
+        assert np.max(np.abs(host(score)[h] - s)) < 1e-4
+
+    idx_in = torch.from_numpy(ridx).to(DEV)
+    for keep_special in (True, False):
+        o_slc = sga.gsa_sparse_attn(q, k, v, idx_in, geom, top_k, keep_special=keep_special,
+                                    keep_ref=True)
+        _sync()
+        want = oracle.fine_attention(qh, kh, vh, geom, 4, ridx, keep_special=keep_special,
+                                     keep_ref=True)
+        assert_close(host(o_slc), want, geom.dtype, f"o_slc (reference frame, specials={keep_special})")
+    if top_k > 1:
+        slipped = idx_in.clone()
+        slipped[..., 0] = 0       # a window of frame 0: must add nothing
+        o_slc = sga.gsa_sparse_attn(q, k, v, slipped, geom, top_k, keep_ref=True)
+        _sync()
+        want = oracle.fine_attention(qh, kh, vh, geom, 4, ridx[..., 1:], keep_ref=True)
+        assert_close(host(o_slc), want, geom.dtype, "o_slc (frame-0 window ignored)")
+    _layer_on_decided_rows(geom, q, k, v, w, b, top_k, True, "gsa layer (reference frame)")
+
+
+@pytest.mark.parametrize("n_special", [0, 1])
+def test_pi3_no_registers(n_special):
+    """The pi^3 adaptation: GSA applied directly, without register tokens (no
+    special token at all, or a single one)."""
+    geom = Geometry(6, n_special, 13, 11, 2, 64, "bf16")
+    _announce(f"pi3 {geom}")
+    q, k, v = make_qkv(geom, seed=43, device=DEV, distribution="scene")
+    w, b = make_gate(geom.n_heads, 64, seed=43, device=DEV)
+    _layer_on_decided_rows(geom, q, k, v, w, b, 8, False, f"gsa layer (S={n_special})")
+
+
 def test_deterministic():
     geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
     _announce(f"determinism {geom}")
@@ -316,16 +399,30 @@ def test_dense32():
                  "dense32 frame")
 
 
-def _gsa_check(name, rows_cap=None):
+def _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, top_k, name, keep_ref=False):
+    """The fine branch and the gate on every sampled row: the fine kernel gets
+    the oracle's index sets for the sampled rows' query blocks (the same input
+    on both sides), so rows whose selection is undecided are checked too."""
+    idx_mix = out["idx"].clone()
+    idx_mix[:, torch.from_numpy(ref["blocks"]).to(DEV)] = torch.from_numpy(ref["idx"]).to(DEV)
+    o_slc = sga.gsa_sparse_attn(q, k, v, idx_mix, geom, top_k, keep_ref=keep_ref)
+    o = sga.gsa_gate(q, out["o_cmp"], o_slc, w, b, geom)
+    _sync()
+    assert_close(host(o_slc)[rows], ref["o_slc"], "bf16", f"{name} o_slc (oracle sets, all rows)")
+    assert_close(host(o)[rows], ref["o"], "bf16", f"{name} gsa layer (oracle sets, all rows)")
+
+
+def _gsa_check(name, rows_cap=None, keep_ref=False):
     wl, geom, q, k, v = _workload_inputs(name)
     w, b = make_gate(geom.n_heads, 64, seed=1, device=DEV)
     rows = sample_rows(geom.n_tokens, rows_cap or wl.check_rows, seed=1).numpy()
-    _announce(f"{name} GSA layer, {len(rows)} rows")
-    out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True)
+    _announce(f"{name} GSA layer (reference frame kept: {keep_ref}), {len(rows)} rows")
+    out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True, keep_ref=keep_ref)
     _sync()
     qh, kh, vh = host(q), host(k), host(v)
     W = oracle_workers()
-    ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), wl.top_k, rows=rows, workers=W)
+    ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), wl.top_k, rows=rows, workers=W,
+                           keep_ref=keep_ref)
     assert_close(host(out["k_cmp"]), ref["k_cmp"], "bf16", f"{name} k_cmp")
     assert_close(host(out["v_cmp"]), ref["v_cmp"], "bf16", f"{name} v_cmp")
     assert_close(host(out["k_cmp_f32"]), ref["k_cmp"], "f32", f"{name} k_cmp_f32")
@@ -342,11 +439,17 @@ def _gsa_check(name, rows_cap=None):
     assert keep.sum() > 0
     assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", f"{name} o_slc")
     assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer")
+    _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, name, keep_ref)
 
 
 @pytest.mark.timeout(900)
 def test_gsa128():
     _gsa_check("gsa128")
+
+
+@pytest.mark.timeout(900)
+def test_gsa128_reference_frame():
+    _gsa_check("gsa128", rows_cap=1024, keep_ref=True)
 
 
 def _sga_check(name, rows_cap=None):
@@ -424,6 +527,7 @@ def test_scene1000_gsa(scene1000):
     assert keep.sum() > 0
     assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", "scene1000 o_slc")
     assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", "scene1000 gsa layer")
+    _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, "scene1000")
 
 
 @pytest.mark.timeout(1200)
