@@ -116,10 +116,14 @@ enum { SGA_KEEP_SPECIAL = 1, SGA_KEEP_REF_FRAME = 2 };
  * score (nullable): [H, N*nqb, top_k] fp32, the score of each idx entry.
  * 1 <= top_k <= min(competing keys, 128); competing keys = N*nb, or (N-1)*nb
  * with SGA_KEEP_REF_FRAME.
+ * ws: sga_workspace_size(geom, SGA_OP_TOPK, top_k, keep, &bytes) bytes: none
+ *   for top_k <= 16; above, the candidate buffers of the threshold-and-sort
+ *   selection (at most 1 GiB) and one flag byte per (head, query block).
  */
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
                            const float* k_cmp_f32, int32_t top_k, int32_t keep,
-                           int32_t* idx, float* score, void* stream);
+                           int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * GSA fine attention (Speed3R section 2.1, selection branch): each query of
@@ -181,12 +185,13 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
                                   const void* k, const void* v, void* o, void* ws,
                                   size_t ws_bytes, void* stream);
 
-enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3 };
+enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4 };
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
  * stride_h, stride_w (covers both modes). SGA_OP_FINE: param0 = keep (the
- * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). */
+ * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). SGA_OP_TOPK:
+ * param0 = top_k, param1 = keep (as gsa_select_topk). */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

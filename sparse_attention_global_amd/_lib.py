@@ -21,6 +21,7 @@ SGA_BF16, SGA_F32 = 0, 1
 SGA_OP_SUBSAMPLED = 1
 SGA_OP_DENSE = 2
 SGA_OP_FINE = 3
+SGA_OP_TOPK = 4
 SGA_KEEP_SPECIAL = 1
 SGA_KEEP_REF_FRAME = 2
 
@@ -49,7 +50,7 @@ def library() -> ctypes.CDLL:
     sig = {
         "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
         "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
-        "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P],
+        "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
         "sga_compact": [G, I32, I32, P, P, P, P, P],
@@ -180,8 +181,18 @@ def keep_flags(keep_special: bool = True, keep_ref: bool = False) -> int:
     return (SGA_KEEP_SPECIAL if keep_special else 0) | (SGA_KEEP_REF_FRAME if keep_ref else 0)
 
 
+def topk_workspace_bytes(geom, top_k: int, dtype_code: int = SGA_BF16, keep_ref: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    g = make_geom(geom, dtype_code)
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_TOPK, top_k,
+                                        keep_flags(False, keep_ref), ctypes.byref(n)),
+           "sga_workspace_size")
+    return n.value
+
+
 def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
-                    want_score: bool = False, dtype_code: int = SGA_BF16, keep_ref: bool = False):
+                    want_score: bool = False, dtype_code: int = SGA_BF16, keep_ref: bool = False,
+                    ws=None):
     """Top-K pooled blocks per (head, query block), ascending; with ``keep_ref``
     frame 0's blocks do not compete (it is kept whole); see include/sga.h."""
     H, d, N = geom.n_heads, 64, geom.n_frames
@@ -192,8 +203,10 @@ def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
     score = torch.empty((H, N * nqb, top_k), dtype=torch.float32,
                         device=q_blk_f32.device) if want_score else None
     g = make_geom(geom, dtype_code)
+    ws = _workspace(topk_workspace_bytes(geom, top_k, dtype_code, keep_ref), q_blk_f32.device, ws)
     _check(library().gsa_select_topk(ctypes.byref(g), block, _ptr(q_blk_f32), _ptr(k_cmp_f32),
                                      top_k, keep_flags(False, keep_ref), _ptr(idx), _ptr(score),
+                                     _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(q_blk_f32)),
            "gsa_select_topk")
     return (idx, score) if want_score else idx

@@ -225,7 +225,7 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, cons
 
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
                            const float* k_cmp_f32, int32_t top_k, int32_t keep, int32_t* idx,
-                           float* score, void* stream) {
+                           float* score, void* ws, size_t ws_bytes, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
@@ -234,8 +234,12 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
   REQUIRE_PTR(k_cmp_f32);
   REQUIRE_PTR(idx);
   REQUIRE_OPT_PTR(score);
+  const size_t need = sga::gsa_topk_workspace(g, top_k);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+  if (need > 0 && !aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
   return from_hip(sga::launch_gsa_topk(g, q_blk_f32, k_cmp_f32, top_k, first_candidate(g, keep), idx,
-                                       score, static_cast<hipStream_t>(stream)),
+                                       score, ws, static_cast<hipStream_t>(stream)),
                   "gsa_select_topk launch");
 }
 
@@ -326,6 +330,11 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
     *bytes = geom->dtype == SGA_BF16 ? sga::flash_bf16_workspace(dense_launch(g, param0, param1)) : 0;
     return SGA_OK;
   }
+  if (op == SGA_OP_TOPK) {
+    if (sga_status st = check_topk(g, param0, param1)) return st;
+    *bytes = sga::gsa_topk_workspace(g, param0);
+    return SGA_OK;
+  }
   if (op == SGA_OP_FINE) {
     if (param1 != 0) return fail(SGA_ERR_INVALID_ARG, "fine workspace: param1 must be 0");
     if (sga_status st = check_keep(g, param0)) return st;
@@ -400,6 +409,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 30000; }
+int32_t sga_version(void) { return 40000; }
 
 }  // extern "C"

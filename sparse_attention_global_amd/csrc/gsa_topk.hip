@@ -48,10 +48,13 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   }
 }
 
+// only (nullable): per (head, query block) flags; a workgroup none of whose
+// blocks is flagged returns at once (the wide kernel's overflow fallback).
 __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __restrict__ q_blk,
                                                        const float* __restrict__ k_cmp,
                                                        long long n_cand, int j0,
                                                        int top_k, int n_rowtiles,
+                                                       const uint8_t* __restrict__ only,
                                                        int32_t* __restrict__ idx,
                                                        float* __restrict__ score) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
   const int hh = lane >> 5, li = lane & 31;
   const long long row = row0 + wave * 32 + li;
   const bool rvalid = row < n_rows;
+  if (only != nullptr && !__syncthreads_or(rvalid && only[(long long)h * n_rows + row] != 0)) return;
 
   // per-row sorted lists: [wave][32 rows][top_k + 1] (padded stride)
   const int stride = top_k + 1;
@@ -465,10 +469,410 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide selection, kRegK < top_k <= 128: bound, filter, sort.
+//
+// 1. Bound (gsa_topk_bound_kernel). Every other 64-key tile is scored; for
+//    each of its 32 score positions in a tile (a fixed residue of the key
+//    index mod 64) a lane keeps the DEPTH largest scores seen: 32*DEPTH values
+//    per lane from disjoint key buckets, all distinct candidates. K distinct
+//    candidates scoring at least x make x a lower bound of the block's K-th
+//    best score, so min(the ceil(K/2)-th value of one lane, the floor(K/2)-th
+//    of the other) is one. DEPTH is 2 up to top-64 and 4 beyond.
+// 2. Filter (gsa_topk_wide_kernel). All keys are scored again; every score at
+//    or above the bound is appended, as a 64-bit key (order-preserving score
+//    bits, then the inverted index, so a larger key is the better candidate
+//    under the tie rule), to the lane's own region of its workgroup's buffer;
+//    the count keeps going past the region.
+// 3. Select (same kernel). One wave per query block loads the block's keys,
+//    sorts them with a bitonic network across the wave (2 to 16 keys per
+//    lane), keeps the first top_k and writes their indices in ascending order.
+// A block with a lane past its region (heavy ties, adversarial scores) is
+// flagged and recomputed afterwards by the LDS-list kernel, which is exact
+// with the same tie rule. The filter kernel is persistent, one workgroup per
+// buffer slot, so the buffer scales with the machine, not with the problem.
+// ---------------------------------------------------------------------------
+constexpr int kWideCap = 512;                      // appended keys per lane
+constexpr int kWideRows = 128;                     // query blocks per workgroup
+constexpr long long kWideMaxSlots = 1024;          // buffer slots (persistent workgroups)
+constexpr long long kWideSlotKeys = (long long)kWideRows * 2 * kWideCap;
+
+// One head's competing pooled keys streamed through LDS in 64-key tiles
+// (double buffered) and scored against each lane's pooled query with the
+// three-term split; visit(s, u0) gets the lane's 32 scores of a tile (keys
+// past the end scored -inf).
+struct ScoreStream {
+  unsigned char* smem;
+  const float* k_cmp;
+  long long n_cand, rs, hoff;
+  int tid, li, hh;
+  u32x4 qh[4], ql[4];
+  f32x4 kreg[4];
+
+  __device__ __forceinline__ void load_q(const float* q_blk, long long row, bool rvalid) {
+    // scaled by 1/sqrt(64) = 1/8 (exact), hi and lo planes
+    const float* qp = q_blk + (rvalid ? row : 0) * rs + hoff + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float x[8];
+      const f32x4 a = *reinterpret_cast<const f32x4*>(qp + ks * 16);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(qp + ks * 16 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = rvalid ? a[e] * 0.125f : 0.f;
+        x[4 + e] = rvalid ? b[e] * 0.125f : 0.f;
+      }
+      split8(x, qh[ks], ql[ks]);
+    }
+  }
+  __device__ __forceinline__ void load_tile(long long u0) {
+    const long long u = u0 + (tid >> 2);
+    const int quarter = tid & 3;
+    if (u < n_cand) {
+      const float* kp = k_cmp + u * rs + hoff + quarter * 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kreg[e] = *reinterpret_cast<const f32x4*>(kp + 4 * e);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kreg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __device__ __forceinline__ void store_tile(int stage) {
+    unsigned char* hi_p = smem + stage * kStageBytes;
+    unsigned char* lo_p = hi_p + kTileBytes;
+    const int key = tid >> 2, quarter = tid & 3;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = kreg[2 * half][e];
+        x[4 + e] = kreg[2 * half + 1][e];
+      }
+      u32x4 hi, lo;
+      split8(x, hi, lo);
+      const int chunk = 2 * quarter + half;
+      st16(hi_p + t_off(key, chunk), hi);
+      st16(lo_p + t_off(key, chunk), lo);
+    }
+  }
+  // tiles it = 0, stride, 2*stride, ... of the key range
+  template <class Visit>
+  __device__ __forceinline__ void run(int stride, Visit&& visit) {
+    const long long n_ktiles = (n_cand + kTileN - 1) / kTileN;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    int stage = 0;
+    for (long long it = 0; it < n_ktiles; it += stride) {
+      const long long u0 = it * kTileN;
+      const bool more = it + stride < n_ktiles;
+      if (more) load_tile(u0 + (long long)stride * kTileN);
+      const unsigned char* hi_p = smem + stage * kStageBytes;
+      const unsigned char* lo_p = hi_p + kTileBytes;
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 ah = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
+          const u32x4 al = ld16(lo_p + t_off(kb * 32 + li, 2 * ks + hh));
+          acc = mfma32(al, qh[ks], acc);
+          acc = mfma32(ah, ql[ks], acc);
+          acc = mfma32(ah, qh[ks], acc);
+        }
+        s[kb] = acc;
+      }
+      if (u0 + kTileN > n_cand) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const long long j = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (j >= n_cand) s[kb][i] = -INFINITY;
+          }
+      }
+      visit(s, u0);
+      if (more) store_tile(stage ^ 1);
+      __syncthreads();
+      stage ^= 1;
+    }
+  }
+};
+
+template <int DEPTH>
+__global__ __launch_bounds__(256, 2) void gsa_topk_bound_kernel(Geom g, const float* __restrict__ q_blk,
+                                                               const float* __restrict__ k_cmp,
+                                                               long long n_cand, int top_k,
+                                                               int n_rowtiles,
+                                                               float* __restrict__ bound) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int V = 32 * DEPTH;  // values per lane
+  const int h = blockIdx.x / n_rowtiles;
+  const long long row0 = (long long)(blockIdx.x % n_rowtiles) * kWideRows;
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  const long long row = row0 + wave * 32 + li;
+  const bool rvalid = row < n_rows;
+
+  ScoreStream st;
+  st.smem = smem;
+  st.k_cmp = k_cmp;
+  st.n_cand = n_cand;
+  st.rs = (long long)g.n_heads * kHeadDim;
+  st.hoff = (long long)h * kHeadDim;
+  st.tid = tid;
+  st.li = li;
+  st.hh = hh;
+  st.load_q(q_blk, row, rvalid);
+
+  // m[d * 32 + p]: the (d+1)-th largest score seen at position p
+  float m[V];
+#pragma unroll
+  for (int p = 0; p < V; ++p) m[p] = -INFINITY;
+  st.run(2, [&](const f32x16 (&s)[2], long long) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int p = kb * 16 + i;
+        float x = s[kb][i];
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {  // x sinks to its place; the smallest falls off
+          const float hi = fmaxf(m[d * 32 + p], x);
+          x = fminf(m[d * 32 + p], x);
+          m[d * 32 + p] = hi;
+        }
+      }
+  });
+  // the c-th largest of the lane's V values, by a bitwise search over their
+  // order-preserving integer images: the largest t with c values >= t
+  uint32_t o[V];
+#pragma unroll
+  for (int p = 0; p < V; ++p) {
+    const uint32_t u = __float_as_uint(m[p]);
+    o[p] = u ^ ((u & 0x80000000u) ? 0xffffffffu : 0x80000000u);
+  }
+  auto kth = [&](int c) {
+    uint32_t t = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int p = 0; p < V; ++p) n += o[p] >= cand ? 1 : 0;
+      t = n >= c ? cand : t;
+    }
+    return __uint_as_float(t ^ ((t & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+  };
+  const float x_hi = kth((top_k + 1) / 2);
+  const float x_lo = kth(top_k / 2);
+  // lane l < 32 contributes its ceil(K/2)-th value, lane l + 32 its floor(K/2)-th
+  const float mine = hh == 0 ? x_hi : x_lo;
+  const float tau = fminf(mine, __shfl_xor(mine, 32, 64));
+  if (rvalid && hh == 0) bound[(long long)h * n_rows + row] = tau;
+}
+
+__device__ __forceinline__ uint64_t order_key(float s, int j) {
+  uint32_t u = __float_as_uint(s);
+  u ^= (u & 0x80000000u) ? 0xffffffffu : 0x80000000u;
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - (uint32_t)j);
+}
+__device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
+__device__ __forceinline__ float key_score(uint64_t key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u ^= (u & 0x80000000u) ? 0x80000000u : 0xffffffffu;
+  return __uint_as_float(u);
+}
+
+// Bitonic sort, descending, of the 64*E keys of a wave held lane-major
+// (key e = lane*E + r in a[r] of lane e/E).
+template <int E>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&a)[E], int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64 * E; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= E) {  // partners in lane ^ (j / E), same register
+        const int lm = j / E;
+        const bool lower = (lane & lm) == 0;
+        const bool desc = ((lane * E) & k) == 0;
+        const bool take_max = lower == desc;
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const uint64_t o = __shfl_xor(a[r], lm, 64);
+          const bool keep = take_max ? (a[r] > o) : (a[r] < o);
+          a[r] = keep ? a[r] : o;
+        }
+      } else {       // partners in the same lane
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int p = r ^ j;
+          if (p > r) {
+            const bool desc = (k >= E) ? (((lane * E) & k) == 0) : ((r & k) == 0);
+            const uint64_t x = a[r], y = a[p];
+            const bool sw = desc ? (x < y) : (x > y);
+            a[r] = sw ? y : x;
+            a[p] = sw ? x : y;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Sorts a query block's n0 + n1 appended keys (E per lane), keeps the first
+// top_k and writes their indices (+ j0) ascending, with their scores.
+template <int E>
+__device__ __forceinline__ void select_block(const uint64_t* __restrict__ rb, int n0, int n1,
+                                             int top_k, int lane, uint64_t* lds, int j0,
+                                             int32_t* __restrict__ ip, float* __restrict__ sp) {
+  uint64_t a[E];
+#pragma unroll
+  for (int r = 0; r < E; ++r) {
+    const int e = lane * E + r;
+    a[r] = e < n0 ? rb[e] : (e < n0 + n1 ? rb[kWideCap + e - n0] : 0ull);
+  }
+  wave_sort_desc<E>(a, lane);
+#pragma unroll
+  for (int r = 0; r < E; ++r)
+    if (lane * E + r < top_k) lds[lane * E + r] = a[r];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int e = lane; e < top_k; e += 64) {
+    const uint64_t key = lds[e];
+    const int j = key_index(key);
+    int pos = 0;
+    for (int f = 0; f < top_k; ++f) pos += key_index(lds[f]) < j ? 1 : 0;
+    ip[pos] = j + j0;
+    if (sp) sp[pos] = key_score(key);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+__global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const float* __restrict__ q_blk,
+                                                              const float* __restrict__ k_cmp,
+                                                              long long n_cand, int j0, int top_k,
+                                                              int n_rowtiles, long long n_tiles,
+                                                              const float* __restrict__ bound,
+                                                              uint64_t* __restrict__ buf,
+                                                              uint8_t* __restrict__ flags,
+                                                              int32_t* __restrict__ idx,
+                                                              float* __restrict__ score) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* sel_lds = reinterpret_cast<uint64_t*>(smem + 2 * kStageBytes);
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  uint64_t* slot = buf + (long long)blockIdx.x * kWideSlotKeys;
+  uint64_t* my_keys = slot + ((long long)(wave * 32 + li) * 2 + hh) * kWideCap;
+  uint64_t* wave_lds = sel_lds + wave * 128;
+
+  ScoreStream st;
+  st.smem = smem;
+  st.k_cmp = k_cmp;
+  st.n_cand = n_cand;
+  st.rs = (long long)g.n_heads * kHeadDim;
+  st.tid = tid;
+  st.li = li;
+  st.hh = hh;
+
+  for (long long t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int h = (int)(t / n_rowtiles);
+    const long long row0 = (t % n_rowtiles) * kWideRows;
+    const long long row = row0 + wave * 32 + li;
+    const bool rvalid = row < n_rows;
+    st.hoff = (long long)h * kHeadDim;
+    st.load_q(q_blk, row, rvalid);
+    const float tau = rvalid ? bound[(long long)h * n_rows + row] : INFINITY;
+
+    // ---- filter: append every score >= tau ------------------------------------
+    int cnt = 0;
+    st.run(1, [&](const f32x16 (&s)[2], long long u0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float sv = s[kb][i];
+          const bool c = sv >= tau && sv > -INFINITY;
+          if (__any(c)) {
+            if (c) {
+              const int j = (int)u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              if (cnt < kWideCap) my_keys[cnt] = order_key(sv, j);
+              ++cnt;
+            }
+          }
+        }
+    });
+    const int other = __shfl_xor(cnt, 32, 64);
+    const bool over = cnt > kWideCap || other > kWideCap || cnt + other < top_k;
+    if (rvalid && hh == 0) flags[(long long)h * n_rows + row] = over ? 1 : 0;
+    // the keys were written by other lanes of this wave, through the vector
+    // caches: make them visible to the loads below
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // ---- select: one query block at a time per wave ---------------------------
+    for (int r = 0; r < 32; ++r) {
+      const long long brow = row0 + wave * 32 + r;
+      if (brow >= n_rows) break;
+      const int n0 = __builtin_amdgcn_readlane(cnt, r);
+      const int n1 = __builtin_amdgcn_readlane(cnt, r + 32);
+      if (n0 > kWideCap || n1 > kWideCap || n0 + n1 < top_k) continue;
+      const uint64_t* rb = slot + (long long)(wave * 32 + r) * 2 * kWideCap;
+      int32_t* ip = idx + ((long long)h * n_rows + brow) * top_k;
+      float* sp = score ? score + ((long long)h * n_rows + brow) * top_k : nullptr;
+      const int n = n0 + n1;
+      if (n <= 128) select_block<2>(rb, n0, n1, top_k, lane, wave_lds, j0, ip, sp);
+      else if (n <= 256) select_block<4>(rb, n0, n1, top_k, lane, wave_lds, j0, ip, sp);
+      else if (n <= 512) select_block<8>(rb, n0, n1, top_k, lane, wave_lds, j0, ip, sp);
+      else select_block<16>(rb, n0, n1, top_k, lane, wave_lds, j0, ip, sp);
+    }
+  }
+}
+
+// Workgroups of a kernel that fit on the device at once.
+int resident_workgroups(const void* kernel, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cus[64] = {0};
+  int n_cu = 256;
+  if (dev >= 0 && dev < 64) {
+    if (cus[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus[dev] = prop.multiProcessorCount;
+    }
+    if (cus[dev] > 0) n_cu = cus[dev];
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu * n_cu;
+}
+
 }  // namespace
 
+static size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t gsa_topk_workspace(const Geom& g, int top_k) {
+  if (top_k <= kRegK) return 0;
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const long long tiles = (n_rows + kWideRows - 1) / kWideRows * g.n_heads;
+  const long long slots = tiles < kWideMaxSlots ? tiles : kWideMaxSlots;
+  return round_up256((size_t)slots * kWideSlotKeys * sizeof(uint64_t)) +
+         round_up256((size_t)(n_rows * g.n_heads) * sizeof(float)) +
+         round_up256((size_t)(n_rows * g.n_heads));
+}
+
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
-                           int first, int32_t* idx, float* score, hipStream_t stream) {
+                           int first, int32_t* idx, float* score, void* ws, hipStream_t stream) {
   const long long n_rows = (long long)g.n_frames * g.nqb;
   // the kernels see the competing keys only, indexed from 0, and add `first`
   // to the indices they write
@@ -487,14 +891,40 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
     }
     return hipGetLastError();
   }
+  // wide: the bound, then filter and sort in a persistent kernel, then the
+  // LDS-list kernel for the blocks it flagged
+  const int n_rowtiles = (int)((n_rows + kWideRows - 1) / kWideRows);
+  const long long tiles = (long long)n_rowtiles * g.n_heads;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long slots = tiles < kWideMaxSlots ? tiles : kWideMaxSlots;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  uint64_t* buf = reinterpret_cast<uint64_t*>(w);
+  w += round_up256((size_t)slots * kWideSlotKeys * sizeof(uint64_t));
+  float* bound = reinterpret_cast<float*>(w);
+  w += round_up256((size_t)(n_rows * g.n_heads) * sizeof(float));
+  uint8_t* flags = reinterpret_cast<uint8_t*>(w);
+  if (top_k <= 64) {
+    hipLaunchKernelGGL(gsa_topk_bound_kernel<2>, dim3((unsigned)tiles), dim3(256), 2 * kStageBytes, stream,
+                       g, q_blk, kc, n_cand, top_k, n_rowtiles, bound);
+  } else {
+    hipLaunchKernelGGL(gsa_topk_bound_kernel<4>, dim3((unsigned)tiles), dim3(256), 2 * kStageBytes, stream,
+                       g, q_blk, kc, n_cand, top_k, n_rowtiles, bound);
+  }
+  if (hipError_t e = hipGetLastError()) return e;
+  const size_t lds_wide = 2 * kStageBytes + 4 * 128 * sizeof(uint64_t);
+  long long grid = resident_workgroups(reinterpret_cast<const void*>(gsa_topk_wide_kernel), 256, lds_wide);
+  if (grid > slots) grid = slots;
+  hipLaunchKernelGGL(gsa_topk_wide_kernel, dim3((unsigned)grid), dim3(256), lds_wide, stream, g, q_blk, kc,
+                     n_cand, first, top_k, n_rowtiles, tiles, bound, buf, flags, idx, score);
+  if (hipError_t e = hipGetLastError()) return e;
   int waves = 4;
   auto lds_for = [&](int w) { return (size_t)2 * kStageBytes + (size_t)w * 32 * (top_k + 1) * 8; };
   if (lds_for(waves) > 160 * 1024) waves = 2;
-  const int n_rowtiles = (int)((n_rows + 32 * waves - 1) / (32 * waves));
-  const long long grid = (long long)n_rowtiles * g.n_heads;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gsa_topk_kernel, dim3((unsigned)grid), dim3(64 * waves), lds_for(waves), stream,
-                     g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
+  const int n_lds_tiles = (int)((n_rows + 32 * waves - 1) / (32 * waves));
+  const long long lds_grid = (long long)n_lds_tiles * g.n_heads;
+  if (lds_grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gsa_topk_kernel, dim3((unsigned)lds_grid), dim3(64 * waves), lds_for(waves), stream,
+                     g, q_blk, kc, n_cand, first, top_k, n_lds_tiles, flags, idx, score);
   return hipGetLastError();
 }
 

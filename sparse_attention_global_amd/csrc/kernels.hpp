@@ -62,9 +62,12 @@ inline long long kept_rows(const Geom& g, int keep) {
 }
 
 // GSA top-K block selection (gsa_topk.hip). Pooled keys first .. N*nb-1
-// compete; idx holds global indices.
+// compete; idx holds global indices. ws: gsa_topk_workspace(g, top_k) bytes
+// (the wide selection's per-workgroup key buffers and overflow flags; none
+// for top_k <= 16).
+size_t gsa_topk_workspace(const Geom& g, int top_k);
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
-                           int first, int32_t* idx, float* score, hipStream_t stream);
+                           int first, int32_t* idx, float* score, void* ws, hipStream_t stream);
 
 // GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32. keep: kKeep* flags.
 // fp32 visits the kept tokens itself. bf16 takes them through o_init/lse_init

@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 30000
+    assert library().sga_version() == 40000
 
 
 def geom(**kw):
@@ -89,17 +89,17 @@ def test_gsa_calls_reject_bad_arguments():
     assert L.gsa_compress(ctypes.byref(g), 4, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
     nb = 2 * 100
     for bad_k in (0, nb + 1, 129):
-        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, 0, FAKE, None, None) == INVALID
+        assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, 0, FAKE, None, None, 0, None) == INVALID
         assert "top_k" in last_error()
     # with the reference frame kept whole only the other frame's 100 blocks compete
-    assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 101, 2, FAKE, None, None) == INVALID
+    assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 101, 2, FAKE, None, None, 0, None) == INVALID
     assert "competing blocks = 100" in last_error()
     assert L.gsa_select_topk(ctypes.byref(geom(n_frames=1)), 4, FAKE, FAKE, 4, 2, FAKE, None,
-                             None) == INVALID
+                             None, 0, None) == INVALID
     assert "2 frames" in last_error()
     for bad_keep in (-1, 4):
         assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 16, bad_keep, FAKE, None,
-                                 None) == INVALID
+                                 None, 0, None) == INVALID
         assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, bad_keep, FAKE, None,
                                  None, 0, None) == INVALID
         assert "keep" in last_error()
@@ -190,6 +190,28 @@ def test_fine_workspace():
         assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, keep, FAKE, None,
                                  None, 0, None) == WORKSPACE
         assert "workspace" in last_error()
+
+
+def test_topk_workspace():
+    g = geom(n_frames=256)
+    n_rows = 256 * 101
+    # top_k <= 16: the register kernel needs nothing
+    assert _ws(g, 4, 16, 0) == (OK, 0)
+    # wider: one 1 MiB key buffer per persistent workgroup (128 blocks x 2 lanes
+    # x 512 keys x 8 bytes), at most 1024 of them, then a score bound (fp32)
+    # and a flag byte per (head, query block)
+    tiles = -(-n_rows // 128) * 16
+    assert _ws(g, 4, 17, 0) == (OK, min(tiles, 1024) * (1 << 20) + r256(n_rows * 16 * 4)
+                                + r256(n_rows * 16))
+    small = geom(n_frames=3, n_heads=2)
+    assert _ws(small, 4, 20, 0) == (OK, 3 * 2 * (1 << 20) + r256(3 * 101 * 2 * 4)
+                                    + r256(3 * 101 * 2))  # 3 row tiles x 2 heads
+    assert _ws(g, 4, 129, 0)[0] == INVALID
+    assert _ws(geom(n_frames=1), 4, 20, 2)[0] == INVALID
+    # a missing workspace is reported before anything is launched
+    assert library().gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 17, 0, FAKE, None, None, 0,
+                                     None) == WORKSPACE
+    assert "workspace" in last_error()
 
 
 def test_python_layer_requires_gpu_tensors():

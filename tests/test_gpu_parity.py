@@ -202,12 +202,13 @@ def test_invariants_on_gpu():
     assert_close(host(o_d), ref, "bf16", "dense")
 
 
-def test_topk_planted_winners():
+@pytest.mark.parametrize("top_k", [16, 100, 128])
+def test_topk_planted_winners(top_k):
     """Designed pooled scores with known, separated winners: block b's pooled
     query is the unit vector of coordinate c_b, so only keys of class c_b score,
     by their planted magnitudes (spaced 0.01 apart, i.e. 1.25e-3 in score)."""
     geom = Geometry(128, 5, 37, 37, 2, 64, "bf16")
-    _announce(f"planted top-K {geom}")
+    _announce(f"planted top-{top_k} {geom}")
     N, H = geom.n_frames, geom.n_heads
     nk, nq = N * _nb(geom), N * _nqb(geom)
     rng = np.random.default_rng(5)
@@ -224,19 +225,20 @@ def test_topk_planted_winners():
     for h in range(H):
         q32[np.arange(nq), h, qc[:, h]] = 1.0
     idx = sga.gsa_select_topk(torch.tensor(q32, dtype=torch.float32, device=DEV),
-                              torch.tensor(k32, dtype=torch.float32, device=DEV), geom, 16)
+                              torch.tensor(k32, dtype=torch.float32, device=DEV), geom, top_k)
     _sync()
     got = host(idx).astype(np.int64)
     for h in range(H):
         for bb in range(0, nq, 97):
             members = np.nonzero(cls == qc[bb, h])[0]
-            want = np.sort(members[np.argsort(-mag[members], kind="stable")[:16]])
+            want = np.sort(members[np.argsort(-mag[members], kind="stable")[:top_k]])
             assert np.array_equal(got[h, bb], want), (h, bb)
 
 
-@pytest.mark.parametrize("top_k", [7, 16, 32, 128])
+@pytest.mark.parametrize("top_k", [7, 16, 17, 32, 64, 100, 128])
 def test_topk_widths(top_k):
-    """Both selection kernels: register lists up to 16, LDS lists beyond."""
+    """Every selection path: register lists up to 16; beyond, the bound /
+    filter / sort kernel (its sorts of 128 to 1024 keys per block)."""
     geom = Geometry(16, 5, 37, 37, 2, 64, "bf16")
     _announce(f"top-K width {top_k} {geom}")
     q, k, v = make_qkv(geom, seed=31, device=DEV, distribution="scene")
@@ -336,6 +338,45 @@ def test_pi3_no_registers(n_special):
     q, k, v = make_qkv(geom, seed=43, device=DEV, distribution="scene")
     w, b = make_gate(geom.n_heads, 64, seed=43, device=DEV)
     _layer_on_decided_rows(geom, q, k, v, w, b, 8, False, f"gsa layer (S={n_special})")
+
+
+def test_topk_wide_ties_fall_back():
+    """Every pooled key equal: every score ties, so the wide selection's
+    filter keeps all 1600 candidates, overflows its buffers and leaves every
+    block to the exact LDS-list kernel; ties go to the lowest indices."""
+    geom = Geometry(16, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"wide top-K, all scores tied {geom}")
+    N, H = geom.n_frames, geom.n_heads
+    rng = np.random.default_rng(7)
+    k32 = np.tile(rng.standard_normal((1, H, 64)), (N * _nb(geom), 1, 1))
+    q32 = rng.standard_normal((N * _nqb(geom), H, 64))
+    for top_k in (17, 100, 128):
+        idx, score = sga.gsa_select_topk(torch.tensor(q32, dtype=torch.float32, device=DEV),
+                                         torch.tensor(k32, dtype=torch.float32, device=DEV), geom,
+                                         top_k, want_score=True)
+        _sync()
+        got = host(idx).astype(np.int64)
+        assert (got == np.arange(top_k)[None, None, :]).all(), top_k
+        ridx, ranked = oracle.select_topk(q32[::37], k32, top_k)
+        assert (ridx == np.arange(top_k)[None, None, :]).all()
+        assert np.max(np.abs(host(score)[:, ::37] - ranked[:, :, :top_k])) < 1e-4
+
+
+def test_topk_wide_few_candidates():
+    """Fewer competing blocks than the bound's 128 buckets: the bound is -inf,
+    every candidate is kept and sorted (3 frames x 12 blocks, top-20; 2 frames
+    with frame 0 kept whole, top-12 of 12)."""
+    geom = Geometry(3, 5, 13, 11, 2, 64, "bf16")
+    _announce(f"wide top-K, few candidates {geom}")
+    q, k, v = make_qkv(geom, seed=51, device=DEV, distribution="scene")
+    _, _, k32, q32 = sga.gsa_compress(q, k, v, geom)
+    rkc, _ = oracle.compress(host(k), host(v), geom, 4)
+    rqb = oracle.pooled_queries(host(q), geom, 4)
+    for top_k, keep_ref in ((20, False), (24, True)):
+        idx = sga.gsa_select_topk(q32, k32, geom, top_k, keep_ref=keep_ref)
+        _sync()
+        ridx, ranked = oracle.select_topk(rqb, rkc, top_k, first=_nb(geom) if keep_ref else 0)
+        check_topk(host(idx).astype(np.int64), ridx, ranked, rqb, rkc, f"top-{top_k} of few")
 
 
 def test_deterministic():
