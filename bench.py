@@ -9,9 +9,11 @@ before timing starts):
 Every kernel of the step is launched on torch's current stream; per-call times
 come from HIP events on that stream over the timed region.
 
-After the timed steps, the Speed3R variants of the GSA layer are timed on the
-same inputs, outside the step: the VGGT adaptation (reference frame 0 kept
-whole, top-16 over the other frames) and the test-time top-128.
+After the timed steps, variants are timed outside the step: the Speed3R GSA
+variants on the same inputs (the VGGT adaptation: reference frame 0 kept
+whole, top-16 over the other frames; the test-time top-128), the AVGGT
+subsampling factor 2..9, and AVGGT's layer schedule (frame attention for the
+early layers, subsampled after) at 100, 300 and 800 frames.
 
 Prints one JSON line. `value` = tokens of the batch / seconds per step.
 """
@@ -196,6 +198,40 @@ def main():
             del ws_v, vidx
             print(f"[bench] variant {vname}: {t_v:.1f} ms", file=sys.stderr, flush=True)
 
+    if args.variant_steps > 0:
+        def timed(fn, reps):
+            """ms per call from HIP events on the current stream; one untimed call first."""
+            fn()
+            t = 0.0
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                t += e0.elapsed_time(e1) / reps
+            return t
+
+        # AVGGT subsampling factor sigma = 2..9 (sigma x sigma windows)
+        sweep = {}
+        for sig in range(2, 10):
+            ws_s = torch.empty(sga.workspace_bytes(geom, sig, sig, sga.SGA_BF16), dtype=torch.uint8,
+                               device=dev)
+            t_s = timed(lambda: sga.subsampled_global_attn(q, k, v, geom, sig, sig, ws=ws_s),
+                        args.variant_steps)
+            mk_s, hm_s = sga.compact_rows(geom, sig, sig)
+            fl_s = 4.0 * T * (geom.tokens_per_frame + (N - 1) * (mk_s + hm_s)) * d * H
+            sweep[str(sig)] = {"ms": t_s, "speedup_vs_dense": per["dense"] / t_s,
+                               "keys_per_query": geom.tokens_per_frame + (N - 1) * (mk_s + hm_s),
+                               "tflops": fl_s / t_s / 1e9,
+                               "mfma_frac": fl_s / t_s / 1e9 / PEAK_BF16_TFLOPS}
+            del ws_s
+        layers["subsampled_sigma_sweep"] = sweep
+        print("[bench] sigma sweep: " + " ".join(f"{k_}:{v_['ms']:.0f}ms" for k_, v_ in sweep.items()),
+              file=sys.stderr, flush=True)
+        layers["avggt_schedule"] = avggt_schedule(sga, torch, make_qkv, geom, wl, dev, timed,
+                                                  args.seed)
+
     achieved = flop_dense / (per["dense"] * 1e-3) / 1e12
     roofline = {"kernel": "flash_bf16_kernel<GLOBAL> (dense global attention)",
                 "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
@@ -224,6 +260,39 @@ def main():
         "layers": layers, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+GLOBAL_LAYERS = 24   # global-attention layers of the model (not stated by the pages; VGGT's depth)
+FRAME_LAYERS = 9     # early global layers turned into frame attention (indices 0-8)
+
+
+def avggt_schedule(sga, torch, make_qkv, geom1000, wl, dev, timed, seed):
+    """AVGGT's two-step schedule over the model's global-attention layers at
+    100, 300 and 800 frames: layers 0-8 as frame attention, the rest as
+    subsampled attention (4x4), against every layer dense. One timed call of
+    each form per size; the per-layer times let any layer count be recomposed."""
+    out = {"global_layers": GLOBAL_LAYERS, "frame_layers": FRAME_LAYERS, "stride": list(wl.stride)}
+    sh, sw = wl.stride
+    for n in (100, 300, 800):
+        g = geom1000.replace(n_frames=n)
+        q, k, v = make_qkv(g, seed=seed, device=dev, distribution=wl.distribution)
+        ws_d = torch.empty(sga.dense_workspace_bytes(g, sga.SGA_BF16), dtype=torch.uint8, device=dev)
+        ws_f = torch.empty(sga.dense_workspace_bytes(g, sga.SGA_BF16, frame_local=True),
+                           dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(sga.workspace_bytes(g, sh, sw, sga.SGA_BF16), dtype=torch.uint8, device=dev)
+        t_d = timed(lambda: sga.dense_global_attn(q, k, v, g, ws=ws_d), 1)
+        t_f = timed(lambda: sga.dense_global_attn(q, k, v, g, frame_local=True, ws=ws_f), 1)
+        t_s = timed(lambda: sga.subsampled_global_attn(q, k, v, g, sh, sw, ws=ws_s), 1)
+        dense_stack = GLOBAL_LAYERS * t_d
+        avggt_stack = FRAME_LAYERS * t_f + (GLOBAL_LAYERS - FRAME_LAYERS) * t_s
+        out[str(n)] = {"dense_ms": t_d, "frame_ms": t_f, "subsampled_ms": t_s,
+                       "dense_stack_ms": dense_stack, "avggt_stack_ms": avggt_stack,
+                       "speedup": dense_stack / avggt_stack}
+        print(f"[bench] avggt schedule at {n} frames: {dense_stack:.0f} ms dense, "
+              f"{avggt_stack:.0f} ms scheduled ({dense_stack / avggt_stack:.1f}x)",
+              file=sys.stderr, flush=True)
+        del q, k, v, ws_d, ws_f, ws_s
+    return out
 
 
 def gsa_rooflines(geom, per, idx, keep_ref=False):

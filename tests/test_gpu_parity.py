@@ -379,6 +379,25 @@ def test_topk_wide_few_candidates():
         check_topk(host(idx).astype(np.int64), ridx, ranked, rqb, rkc, f"top-{top_k} of few")
 
 
+@pytest.mark.parametrize("sigma", range(2, 10))
+def test_subsampled_sigma(sigma):
+    """AVGGT's subsampling factor over its tested range (sigma x sigma windows,
+    2..9), every row of a 6-frame scene, with and without the log-count bias."""
+    geom = Geometry(6, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"subsampled sigma={sigma} {geom}")
+    q, k, v = make_qkv(geom, seed=60 + sigma, device=DEV, distribution="scene")
+    o = sga.subsampled_global_attn(q, k, v, geom, sigma, sigma)
+    ol = sga.subsampled_global_attn(q, k, v, geom, sigma, sigma, mean_log_count=True)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    W = oracle_workers()
+    assert_close(host(o), oracle.subsampled_attention(qh, kh, vh, geom, sigma, sigma, workers=W),
+                 "bf16", f"subsampled sigma={sigma}")
+    assert_close(host(ol), oracle.subsampled_attention(qh, kh, vh, geom, sigma, sigma,
+                                                       mean_log_count=True, workers=W),
+                 "bf16", f"subsampled sigma={sigma} log-count")
+
+
 def test_deterministic():
     geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
     _announce(f"determinism {geom}")
