@@ -46,7 +46,11 @@ R15 the VGGT adaptation of the selection branch ([Speed3R-ja] section 2.2,
     -- frame 0, whose camera fixes VGGT's world coordinates -- whole: every
     query's fine branch attends to all tokens of frame 0, and the top-K is
     taken over the pooled blocks of the other frames only, so that no token is
-    counted twice.
+    counted twice;
+R17 AVGGT's "diagonal" read at token level (the alternative to R9, mode 2):
+    the query's own frame is subsampled like every other frame (its compacted
+    set and mean token included), and the query's own key/value is added when
+    its patch was dropped; the means stay per frame, over all dropped patches.
 
 Arrays are ``[rows, H, d]`` of any float dtype; every computation widens them
 to fp64 first.
@@ -453,10 +457,14 @@ def subsampled_attention(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
     """Subsampled global attention ([AVGGT] section 2.2): every query is kept;
     a query of frame f attends to all of frame f (R9) and to the compacted set
     of every other frame. ``mode`` 1 is the frame-attention conversion of the
-    early layers. With ``mean_log_count`` the mean key's logit gets
-    log(#dropped) added (it then stands for the sum of the dropped columns)."""
+    early layers; ``mode`` 2 the token-level diagonal (R17). With
+    ``mean_log_count`` the mean key's logit gets log(#dropped) added (it then
+    stands for the sum of the dropped columns)."""
     if mode == 1:
         return frame_attention(q, k, v, geom, rows=rows)
+    if mode == 2:
+        return _subsampled_token_diagonal(q, k, v, geom, s_h, s_w, mean_log_count, rows, chunk,
+                                          workers)
     T, H, d = k.shape
     L = _frame_len(geom)
     N = geom.n_frames
@@ -494,6 +502,46 @@ def subsampled_attention(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
             p_c = np.exp(s_c - mx)
             num = np.einsum("il,ild->id", p_own, v_own) + p_c @ cvh
             o[idx] = num / (p_own.sum(axis=1) + p_c.sum(axis=1))[:, None]
+        return o
+
+    return np.stack(head_map(one_head, H, workers), axis=1)
+
+
+def _subsampled_token_diagonal(q, k, v, geom, s_h, s_w, mean_log_count, rows, chunk, workers):
+    """R17: the compacted set of every frame, the query's own frame included,
+    plus the query's own key/value when its patch was dropped; one softmax
+    over the union per query."""
+    T, H, d = k.shape
+    L = _frame_len(geom)
+    N = geom.n_frames
+    rows = _rows(rows, T)
+    kept, dropped = subsample_plan(geom, s_h, s_w)
+    m = geom.n_special + len(kept) + (1 if dropped else 0)
+    ck, cv = sga_compact(k, v, geom, s_h, s_w)
+    bias_c = np.zeros(N * m)
+    if dropped and mean_log_count:
+        bias_c[m - 1::m] = math.log(len(dropped))
+    was_dropped = np.zeros(L, dtype=bool)
+    was_dropped[dropped] = True
+    diag = was_dropped[rows % L]          # the query's own column is not in its frame's compacted set
+    scale = 1.0 / math.sqrt(d)
+
+    def one_head(h):
+        o = np.empty((len(rows), d))
+        ckh = np.ascontiguousarray(ck[:, h, :], np.float64)
+        cvh = np.ascontiguousarray(cv[:, h, :], np.float64)
+        for a in range(0, len(rows), chunk):
+            idx = np.arange(a, min(a + chunk, len(rows)))
+            qc = np.asarray(q[rows[idx], h, :], np.float64)
+            kd = np.asarray(k[rows[idx], h, :], np.float64)
+            vd = np.asarray(v[rows[idx], h, :], np.float64)
+            s_c = (qc @ ckh.T) * scale + bias_c
+            s_d = np.where(diag[idx], np.einsum("id,id->i", qc, kd) * scale, -np.inf)
+            mx = np.maximum(s_c.max(axis=1), s_d)
+            p_c = np.exp(s_c - mx[:, None])
+            p_d = np.exp(s_d - mx)
+            num = p_c @ cvh + p_d[:, None] * vd
+            o[idx] = num / (p_c.sum(axis=1) + p_d)[:, None]
         return o
 
     return np.stack(head_map(one_head, H, workers), axis=1)

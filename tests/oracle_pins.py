@@ -528,4 +528,40 @@ def pin_sga_vs_explicit_keys():
             _close(o[t, h], p @ np.array(vals) / p.sum(), 1e-12)
 
 
+
+def pin_sga_token_diagonal_vs_explicit_keys():
+    """The token-level diagonal reading (mode 2) equals attention over an
+    explicitly enumerated key list: per frame, own frame included, its
+    specials, its kept patches and the mean of its dropped patches (with
+    log(#dropped) on the mean's logit when asked), plus the query's own key
+    when its patch was dropped."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 26)
+    Lf = g.tokens_per_frame
+    d = g.head_dim
+    for log_count in (False, True):
+        o = L.subsampled_attention(q, k, v, g, 2, 3, mode=2, mean_log_count=log_count)
+        for t in range(0, g.n_tokens, 2):
+            for h in range(g.n_heads):
+                keys, vals, bias = [], [], []
+                for u in range(g.n_tokens):
+                    pu = u % Lf
+                    rr, cc = divmod(pu - g.n_special, g.grid_w)
+                    if pu < g.n_special or (rr % 2 == 0 and cc % 3 == 0) or u == t:
+                        keys.append(k[u, h]); vals.append(v[u, h]); bias.append(0.0)
+                for fu in range(g.n_frames):
+                    drop = [fu * Lf + g.n_special + rr * g.grid_w + cc for rr in range(g.grid_h)
+                            for cc in range(g.grid_w) if rr % 2 or cc % 3]
+                    keys.append(k[drop, h].mean(axis=0)); vals.append(v[drop, h].mean(axis=0))
+                    bias.append(math.log(len(drop)) if log_count else 0.0)
+                s_ = np.array(keys) @ q[t, h] / math.sqrt(d) + np.array(bias)
+                p_ = np.exp(s_ - s_.max())
+                _close(o[t, h], p_ @ np.array(vals) / p_.sum(), 1e-12)
+
+
+def pin_sga_token_diagonal_stride1_is_dense():
+    """Stride 1x1 drops nothing: the token-level diagonal reading is dense."""
+    q, k, v = _qkv(G_SMALL, 27)
+    _close(L.subsampled_attention(q, k, v, G_SMALL, 1, 1, mode=2), L.dense_attention(q, k, v), 1e-12)
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

@@ -52,6 +52,14 @@ MUTATIONS = [
     ("sga_mean_token_dropped", "sga_compact", "        if dropped:\n", "        if False:\n"),
     ("sga_log_count_wrong", "subsampled_attention", "math.log(len(dropped))",
      "math.log(len(dropped) + 1)"),
+    ("diag_never_added", "_subsampled_token_diagonal", "diag = was_dropped[rows % L]",
+     "diag = np.zeros(len(rows), dtype=bool)"),
+    ("diag_always_added", "_subsampled_token_diagonal", "diag = was_dropped[rows % L]",
+     "diag = np.ones(len(rows), dtype=bool)"),
+    ("diag_no_log_count", "_subsampled_token_diagonal", "bias_c[m - 1::m] = math.log(len(dropped))",
+     "pass"),
+    ("diag_own_frame_masked", "_subsampled_token_diagonal", "s_c = (qc @ ckh.T) * scale + bias_c",
+     "s_c = (qc @ ckh.T) * scale + bias_c; s_c[:, :m] = -np.inf"),
 ]
 
 
