@@ -227,6 +227,17 @@ def main():
                                "mfma_frac": fl_s / t_s / 1e9 / PEAK_BF16_TFLOPS}
             del ws_s
         layers["subsampled_sigma_sweep"] = sweep
+        # AVGGT's diagonal read at token level (mode 2), at the workload's stride
+        ws_td = torch.empty(sga.workspace_bytes(geom, sh, sw, sga.SGA_BF16), dtype=torch.uint8,
+                            device=dev)
+        t_td = timed(lambda: sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=2, ws=ws_td),
+                     args.variant_steps)
+        fl_td = 4.0 * T * N * (mk + has_mean) * d * H
+        layers["subsampled_token_diagonal"] = {
+            "ms": t_td, "speedup_vs_dense": per["dense"] / t_td, "tflops": fl_td / t_td / 1e9,
+            "mfma_frac": fl_td / t_td / 1e9 / PEAK_BF16_TFLOPS}
+        del ws_td
+        print(f"[bench] token-diagonal subsampled: {t_td:.1f} ms", file=sys.stderr, flush=True)
         print("[bench] sigma sweep: " + " ".join(f"{k_}:{v_['ms']:.0f}ms" for k_, v_ in sweep.items()),
               file=sys.stderr, flush=True)
         layers["avggt_schedule"] = avggt_schedule(sga, torch, make_qkv, geom, wl, dev, timed,

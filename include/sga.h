@@ -174,7 +174,9 @@ sga_status sga_compact(const sga_geom* geom, int32_t stride_h, int32_t stride_w,
  * AVGGT subsampled global attention (AVGGT section 2.2): every query is kept;
  * a query of frame f attends to every token of frame f and to the compacted
  * set of every other frame (sga_compact). mode 1 is the frame-attention
- * conversion of the early layers. With
+ * conversion of the early layers. mode 2 reads the kept diagonal at token
+ * level: a query attends to the compacted set of every frame, its own frame
+ * included, plus its own key/value when its patch was dropped. With
  * mean_log_count == 1 the mean token's logit gets log(#dropped) added.
  * ws: sga_workspace_size(geom, SGA_OP_SUBSAMPLED, stride_h, stride_w, &bytes)
  * bytes: the compacted keys and values (sga_compact layout, each region
@@ -189,7 +191,7 @@ enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
- * stride_h, stride_w (covers both modes). SGA_OP_FINE: param0 = keep (the
+ * stride_h, stride_w (covers every mode). SGA_OP_FINE: param0 = keep (the
  * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). SGA_OP_TOPK:
  * param0 = top_k, param1 = keep (as gsa_select_topk). */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,

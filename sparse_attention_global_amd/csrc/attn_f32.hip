@@ -22,6 +22,8 @@ struct F32Args {
   int mk;
   int has_mean;
   float mean_bias;  // natural-log units
+  int token_diag;   // SUBSAMPLED: own frame subsampled too, plus the query's own key if dropped
+  int s_h, s_w;
 };
 
 __global__ __launch_bounds__(64) void flash_f32_kernel(F32Args A) {
@@ -48,19 +50,26 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(F32Args A) {
   if (A.mode == FLASH_GLOBAL) {
     for (long long u = 0; u < A.n_keys; ++u) visit(A.k + u * rs + hoff, A.v + u * rs + hoff, 0.f);
   } else {
+    const bool diag = A.mode == FLASH_SUBSAMPLED && A.token_diag;
     const long long f0 = (long long)f * A.g.L;
-    for (long long u = f0; u < f0 + A.g.L; ++u) visit(A.k + u * rs + hoff, A.v + u * rs + hoff, 0.f);
+    if (!diag)
+      for (long long u = f0; u < f0 + A.g.L; ++u) visit(A.k + u * rs + hoff, A.v + u * rs + hoff, 0.f);
     if (A.mode == FLASH_SUBSAMPLED) {
       for (long long r = 0; r < (long long)A.g.n_frames * A.mk; ++r) {
-        if (r / A.mk == f) continue;
+        if (!diag && r / A.mk == f) continue;
         visit(A.ck + r * rs + hoff, A.cv + r * rs + hoff, 0.f);
       }
       if (A.has_mean)
         for (int g2 = 0; g2 < A.g.n_frames; ++g2) {
-          if (g2 == f) continue;
+          if (!diag && g2 == f) continue;
           const long long r = (long long)A.g.n_frames * A.mk + g2;
           visit(A.ck + r * rs + hoff, A.cv + r * rs + hoff, A.mean_bias);
         }
+      if (diag) {  // the query's own key when its patch was dropped
+        const int p = (int)(t - f0) - A.g.n_special;
+        if (p >= 0 && ((p / A.g.grid_w) % A.s_h != 0 || (p % A.g.grid_w) % A.s_w != 0))
+          visit(A.k + t * rs + hoff, A.v + t * rs + hoff, 0.f);
+      }
     }
   }
   float* op = A.o + t * rs + hoff;
@@ -85,6 +94,9 @@ hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream) {
   A.mk = p.mk;
   A.has_mean = p.has_mean;
   A.mean_bias = p.mean_bias2 * 0.6931471805599453f;
+  A.token_diag = p.token_diag;
+  A.s_h = p.s_h > 0 ? p.s_h : 1;
+  A.s_w = p.s_w > 0 ? p.s_w : 1;
   dim3 grid((unsigned)((p.g.T + 63) / 64), (unsigned)p.g.n_heads);
   hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(64), 0, stream, A);
   return hipGetLastError();

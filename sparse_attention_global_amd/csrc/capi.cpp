@@ -359,7 +359,8 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(o);
-  if (mode != 0 && mode != 1) return fail(SGA_ERR_INVALID_ARG, "mode must be 0 (subsampled) or 1 (frame)");
+  if (mode < 0 || mode > 2)
+    return fail(SGA_ERR_INVALID_ARG, "mode must be 0 (subsampled), 1 (frame) or 2 (token diagonal)");
   if (mean_log_count != 0 && mean_log_count != 1)
     return fail(SGA_ERR_INVALID_ARG, "mean_log_count must be 0 or 1");
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -403,6 +404,21 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
   p.ck = c_k;
   p.cv = c_v;
   p.mean_bias2 = (mean_log_count && n_drop > 0) ? (float)std::log2((double)n_drop) : 0.f;
+  p.token_diag = mode == 2 ? 1 : 0;
+  p.s_h = stride_h;
+  p.s_w = stride_w;
+  if (mode == 2 && bf && n_drop > 0) {
+    // the compacted sets through the attention kernel, which then leaves the
+    // log-sum-exp in the part of its workspace that holds the whole frames'
+    // V^T in mode 0 (unused here, and larger than T * H floats); the dropped
+    // queries then merge their own key
+    unsigned char* flash_ws = c_k + 2 * half;
+    p.lse = reinterpret_cast<float*>(flash_ws);
+    if (hipError_t e = sga::launch_flash_bf16(p, flash_ws, s))
+      return from_hip(e, "subsampled_global_attn launch");
+    return from_hip(sga::launch_sga_diag_merge(g, stride_h, stride_w, q, k, v, o, p.lse, s),
+                    "subsampled_global_attn (diagonal) launch");
+  }
   return from_hip(bf ? sga::launch_flash_bf16(p, c_k + 2 * half, s) : sga::launch_flash_f32(p, s),
                   "subsampled_global_attn launch");
 }

@@ -101,6 +101,7 @@ struct FlashArgs {
   int mk;            // SUBSAMPLED: kept rows per frame
   int has_mean;      // SUBSAMPLED: one mean row per frame follows the kept part
   float mean_bias2;  // SUBSAMPLED: log2(#dropped) added to mean rows' logits, or 0
+  int token_diag;    // SUBSAMPLED: 1 = no whole own frame; own compacted rows and mean kept
   float bound_extra; // added to every query's logit bound: mean_bias2 if mean rows exist
   const float* knorm2;  // [H, kNormChunks] maxima of |k|^2
   unsigned char* redo;  // [n_logical] 1: the workgroup's rows need the exact pass
@@ -185,17 +186,21 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
 
   // ---- key segments ----------------------------------------------------------
   Segment seg0, seg1;
+  const bool token_diag = MODE == MODE_SUBSAMPLED && A.token_diag != 0;
   if (MODE == MODE_GLOBAL) {
     seg0 = Segment{A.k, 0, A.vt, 0, A.vt_ld, A.n_keys};
   } else {
-    seg0 = Segment{A.k, (long long)f * A.g.L, A.vt, (long long)f * A.vt_pitch, A.vt_ld, A.g.L};
+    seg0 = Segment{A.k, (long long)f * A.g.L, A.vt, (long long)f * A.vt_pitch, A.vt_ld,
+                   token_diag ? 0 : A.g.L};
   }
   seg1 = Segment{A.ck, 0, A.cvt, 0, A.cvt_ld,
                  MODE == MODE_SUBSAMPLED ? (long long)A.g.n_frames * (A.mk + A.has_mean) : 0};
   const long long nt0 = (seg0.n + kTileKeys - 1) / kTileKeys;
   const long long n_tiles = nt0 + (seg1.n + kTileKeys - 1) / kTileKeys;
-  // compacted rows of the own frame (masked), the mean rows (log-count bias)
-  const long long own0 = (long long)f * A.mk, own1 = own0 + A.mk;
+  // compacted rows of the own frame (masked unless token_diag), the mean rows
+  // (log-count bias)
+  const long long own0 = token_diag ? 0 : (long long)f * A.mk;
+  const long long own1 = token_diag ? 0 : own0 + A.mk;
   const long long mean0 = (long long)A.g.n_frames * A.mk;
 
   const int tid = threadIdx.x;
@@ -286,7 +291,7 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
       own_a = rel(own0);
       own_b = rel(own1);
       if (A.has_mean) {
-        own_mean = rel(mean0 + f);
+        own_mean = token_diag ? -1 : rel(mean0 + f);
         mean_a = rel(mean0);
       }
     }
@@ -499,6 +504,7 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   A.mk = p.mk;
   A.has_mean = p.has_mean;
   A.mean_bias2 = p.mean_bias2;
+  A.token_diag = p.token_diag;
   A.scale_log2 = kLog2e / sqrtf((float)kHeadDim);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   bf16* vt = reinterpret_cast<bf16*>(wsb);
@@ -514,8 +520,10 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
     A.remap = 0;
   } else {
     A.vt_pitch = (p.g.L + 63) / 64 * 64;
-    e = launch_vt_prepare(p.v, p.g.n_heads, p.g.T, p.g.L, A.vt_pitch, A.vt_ld, vt, stream);
-    if (e != hipSuccess) return e;
+    if (!(p.mode == FLASH_SUBSAMPLED && p.token_diag)) {  // token_diag reads no whole frame
+      e = launch_vt_prepare(p.v, p.g.n_heads, p.g.T, p.g.L, A.vt_pitch, A.vt_ld, vt, stream);
+      if (e != hipSuccess) return e;
+    }
     if (p.mode == FLASH_SUBSAMPLED) {
       const long long rows = (long long)p.g.n_frames * (p.mk + p.has_mean);
       A.cvt_ld = vt_ld_compact(p);

@@ -27,6 +27,9 @@ struct FlashLaunch {
   int mk;            // SUBSAMPLED: kept rows per frame
   int has_mean;      // SUBSAMPLED: one mean row per frame follows the kept part
   float mean_bias2;  // SUBSAMPLED: log2(#dropped) or 0
+  int token_diag;    // SUBSAMPLED: 1 = the own frame is subsampled like the others (its
+                     // compacted rows and mean kept); the query's own key is not added here
+  int s_h, s_w;      // SUBSAMPLED, token_diag (fp32): the strides, to find dropped queries
 };
 
 // bf16 MFMA flash attention (flash_bf16.hip). ws holds the V^T staging of the
@@ -92,5 +95,10 @@ hipError_t launch_gsa_gate(const Geom& g, bool is_bf16, const void* q, const voi
 // AVGGT compaction (sga_compact.hip): kept part [N*mk,H,d], then mean rows [N,H,d].
 hipError_t launch_sga_compact(const Geom& g, bool is_bf16, int s_h, int s_w, const void* k,
                               const void* v, void* c_k, void* c_v, hipStream_t stream);
+// AVGGT token-level diagonal, bf16 (sga_compact.hip): every query whose patch
+// was dropped (r % s_h or c % s_w nonzero) merges its own key/value into its
+// normalised output o and log-sum-exp lse (natural log) over the rest.
+hipError_t launch_sga_diag_merge(const Geom& g, int s_h, int s_w, const void* q, const void* k,
+                                 const void* v, void* o, const float* lse, hipStream_t stream);
 
 }  // namespace sga

@@ -91,7 +91,62 @@ __global__ __launch_bounds__(256) void sga_compact_kernel(Geom g, int s_h, int s
   Chunk8<T>::store(c_v + dst * rs + col, sv);
 }
 
+// Token-level diagonal (AVGGT technical summary section 2.2, the diagonal
+// kept): a query whose patch was dropped adds its own key/value to the
+// softmax it already has over the compacted sets, given as the normalised
+// output o and the log-sum-exp lse: o' = (e^lse o + e^s v_t) / (e^lse + e^s),
+// s = q_t . k_t / sqrt(d). Eight lanes per (token, head), 16 bytes each.
+__global__ __launch_bounds__(256) void sga_diag_merge_kernel(Geom g, int s_h, int s_w,
+                                                             const u32x4* __restrict__ q,
+                                                             const u32x4* __restrict__ k,
+                                                             const u32x4* __restrict__ v,
+                                                             u32x4* __restrict__ o,
+                                                             const float* __restrict__ lse) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)g.T * g.n_heads * 8) return;
+  const long long th = i >> 3;
+  const long long t = th / g.n_heads;
+  const int h = (int)(th % g.n_heads);
+  const int p = (int)(t % g.L) - g.n_special;
+  // the 8 lanes of a (token, head) take the same branch
+  if (p < 0) return;                                             // a special token: kept
+  if ((p / g.grid_w) % s_h == 0 && (p % g.grid_w) % s_w == 0) return;  // a kept patch
+  const u32x4 qa = q[i], ka = k[i];
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dot = fmaf(lo_bf16(qa[e]), lo_bf16(ka[e]), dot);
+    dot = fmaf(hi_bf16(qa[e]), hi_bf16(ka[e]), dot);
+  }
+  dot += __shfl_xor(dot, 1, 8);
+  dot += __shfl_xor(dot, 2, 8);
+  dot += __shfl_xor(dot, 4, 8);
+  const float s = dot * 0.125f;  // 1/sqrt(64)
+  const float l0 = lse[t * g.n_heads + h];
+  const float mx = fmaxf(l0, s);
+  const float a = expf(l0 - mx), b = expf(s - mx);
+  const float inv = 1.f / (a + b);
+  const u32x4 oa = o[i], va = v[i];
+  u32x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    out[e] = pack_bf16x2((lo_bf16(oa[e]) * a + lo_bf16(va[e]) * b) * inv,
+                         (hi_bf16(oa[e]) * a + hi_bf16(va[e]) * b) * inv);
+  o[i] = out;
+}
+
 }  // namespace
+
+hipError_t launch_sga_diag_merge(const Geom& g, int s_h, int s_w, const void* q, const void* k,
+                                 const void* v, void* o, const float* lse, hipStream_t stream) {
+  const long long n = (long long)g.T * g.n_heads * 8;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sga_diag_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, s_h, s_w,
+                     static_cast<const u32x4*>(q), static_cast<const u32x4*>(k),
+                     static_cast<const u32x4*>(v), static_cast<u32x4*>(o), lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_sga_compact(const Geom& g, bool is_bf16, int s_h, int s_w, const void* k,
                               const void* v, void* c_k, void* c_v, hipStream_t stream) {

@@ -113,7 +113,8 @@ def test_subsampled_rejects_bad_arguments():
     g = geom()
     args = (FAKE, FAKE, FAKE, FAKE)
     assert L.subsampled_global_attn(ctypes.byref(g), 0, 4, 0, 0, *args, FAKE, 1 << 30, None) == INVALID
-    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 2, 0, *args, FAKE, 1 << 30, None) == INVALID
+    assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 3, 0, *args, FAKE, 1 << 30, None) == INVALID
+    assert "token diagonal" in last_error()
     assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 3, *args, FAKE, 1 << 30, None) == INVALID
     assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 0, *args, None, 0, None) == WORKSPACE
     assert L.subsampled_global_attn(ctypes.byref(g), 4, 4, 0, 0, *args, FAKE, 16, None) == WORKSPACE

@@ -398,6 +398,34 @@ def test_subsampled_sigma(sigma):
                  "bf16", f"subsampled sigma={sigma} log-count")
 
 
+@pytest.mark.parametrize("geom,stride", [
+    pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), (4, 4), id="ragged-bf16"),
+    pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), (3, 2), id="ragged-f32"),
+    pytest.param(Geometry(1, 1, 5, 7, 1, 64, "bf16"), (2, 3), id="one-frame-bf16"),
+    pytest.param(Geometry(6, 5, 37, 37, 2, 64, "bf16"), (4, 4), id="scene-bf16"),
+    pytest.param(Geometry(2, 0, 8, 8, 2, 64, "bf16"), (1, 1), id="stride1-bf16"),
+])
+def test_subsampled_token_diagonal(geom, stride):
+    """AVGGT's diagonal read at token level (mode 2): every frame subsampled,
+    the query's own key added when its patch was dropped; every row, with and
+    without the log-count bias; stride 1 is dense attention."""
+    _announce(f"subsampled token diagonal {geom} stride={stride}")
+    dist = "normal" if geom.dtype == "f32" else "scene"
+    q, k, v = make_qkv(geom, seed=71, device=DEV, distribution=dist)
+    sh, sw = stride
+    o = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=2)
+    ol = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=2, mean_log_count=True)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    assert_close(host(o), oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, mode=2), geom.dtype,
+                 "token diagonal")
+    assert_close(host(ol), oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, mode=2,
+                                                       mean_log_count=True), geom.dtype,
+                 "token diagonal log-count")
+    if stride == (1, 1):
+        assert_close(host(o), oracle.dense_attention(qh, kh, vh), geom.dtype, "token diagonal stride 1")
+
+
 def test_deterministic():
     geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
     _announce(f"determinism {geom}")
@@ -519,11 +547,15 @@ def _sga_check(name, rows_cap=None):
     sh, sw = wl.stride
     o = sga.subsampled_global_attn(q, k, v, geom, sh, sw)
     of = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=1)
+    od = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=2)
     _sync()
     qh, kh, vh = host(q), host(k), host(v)
     W = oracle_workers()
     assert_close(host(o)[rows], oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, rows=rows,
                                                             workers=W), "bf16", f"{name} subsampled")
+    assert_close(host(od)[rows], oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, mode=2,
+                                                             rows=rows, workers=W), "bf16",
+                 f"{name} subsampled token diagonal")
     assert_close(host(of)[rows], oracle.frame_attention(qh, kh, vh, geom, rows=rows), "bf16",
                  f"{name} frame")
 
