@@ -50,7 +50,10 @@ R15 the VGGT adaptation of the selection branch ([Speed3R-ja] section 2.2,
 R17 AVGGT's "diagonal" read at token level (the alternative to R9, mode 2):
     the query's own frame is subsampled like every other frame (its compacted
     set and mean token included), and the query's own key/value is added when
-    its patch was dropped; the means stay per frame, over all dropped patches.
+    its patch was dropped; the means stay per frame, over all dropped patches;
+R18 the compressed branch read at block level (the alternative to R1): each
+    query block's mean query attends over the pooled keys/values and every
+    token of the block takes that output (nearest upsampling).
 
 Arrays are ``[rows, H, d]`` of any float dtype; every computation widens them
 to fp64 first.
@@ -66,6 +69,7 @@ import numpy as np
 __all__ = [
     "attend", "attend_union", "dense_attention", "frame_attention", "window_table",
     "query_block_table", "compress", "pooled_queries", "compressed_attention",
+    "compressed_attention_pooled",
     "block_scores", "select_topk", "fine_key_rows", "fine_attention", "gate",
     "gsa_layer", "subsample_plan", "sga_compact", "subsampled_attention",
     "head_map",
@@ -266,6 +270,24 @@ def compressed_attention(q, k_cmp, v_cmp, rows=None, chunk: int = 256, workers=N
     return dense_attention(q, k_cmp, v_cmp, rows=rows, chunk=chunk, workers=workers)
 
 
+def compressed_attention_pooled(q, k_cmp, v_cmp, geom, block: int = 4, rows=None, workers=None):
+    """The compressed branch at block level (R18): the mean query of every
+    query block (R3) attends over all pooled keys/values; each token takes its
+    block's output, i.e. the coarse result upsampled to full resolution by
+    nearest neighbour ([Speed3R-ja] section 2.1, compression branch)."""
+    T = q.shape[0]
+    rows = _rows(rows, T)
+    qbt = query_block_table(geom, block)
+    owner = np.empty(T, dtype=np.int64)
+    for b, members in enumerate(qbt):
+        owner[members] = b
+    need = np.unique(owner[rows])
+    o_blk = dense_attention(pooled_queries(q, geom, block, blocks=need), k_cmp, v_cmp,
+                            workers=workers)
+    pos = np.searchsorted(need, owner[rows])
+    return o_blk[pos]
+
+
 # ---------------------------------------------------------------------------
 # Global Sparse Attention: selection branch
 # ---------------------------------------------------------------------------
@@ -388,15 +410,18 @@ def gate(q, o_cmp, o_slc, w, b):
 
 
 def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
-              keep_special=True, workers=None, keep_ref=False):
+              keep_special=True, workers=None, keep_ref=False, pooled_q=False):
     """The whole Global Sparse Attention layer for the query rows ``rows``:
     pool, compressed branch, block scores + top-K, fine branch, gate.
-    ``keep_ref`` is the VGGT adaptation (R15). Returns a dict with every
-    intermediate."""
+    ``keep_ref`` is the VGGT adaptation (R15); ``pooled_q`` the block-level
+    compressed branch (R18). Returns a dict with every intermediate."""
     T = q.shape[0]
     rows = _rows(rows, T)
     k_cmp, v_cmp = compress(k, v, geom, block)
-    o_cmp = compressed_attention(q, k_cmp, v_cmp, rows=rows, workers=workers)
+    if pooled_q:
+        o_cmp = compressed_attention_pooled(q, k_cmp, v_cmp, geom, block, rows=rows, workers=workers)
+    else:
+        o_cmp = compressed_attention(q, k_cmp, v_cmp, rows=rows, workers=workers)
     qbt = query_block_table(geom, block)
     owner = np.empty(T, dtype=np.int64)
     for bi, members in enumerate(qbt):

@@ -564,4 +564,41 @@ def pin_sga_token_diagonal_stride1_is_dense():
     q, k, v = _qkv(G_SMALL, 27)
     _close(L.subsampled_attention(q, k, v, G_SMALL, 1, 1, mode=2), L.dense_attention(q, k, v), 1e-12)
 
+
+def pin_pooled_compressed_equal_queries():
+    """Block-level compressed branch (R18): when every token of a query block
+    carries the same query, it equals the token-level branch."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 28)
+    for members in L.query_block_table(g, 4):
+        q[members] = q[members[0]]
+    kc, vc = L.compress(k, v, g, 4)
+    _close(L.compressed_attention_pooled(q, kc, vc, g, 4), L.compressed_attention(q, kc, vc), 1e-13)
+
+
+def pin_pooled_compressed_vs_sdpa():
+    """Block-level compressed branch (R18) against torch SDPA over the pooled
+    keys for each block's mean query, formed token by token from the grid
+    (4x4 windows clipped to the grid, a frame's specials as one block), then
+    copied to every token of the block; also on a row subset."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 29)
+    kc, vc = L.compress(k, v, g, 4)
+    o = L.compressed_attention_pooled(q, kc, vc, g, 4)
+    Lf, S = g.tokens_per_frame, g.n_special
+    for h in range(g.n_heads):
+        for t in range(g.n_tokens):
+            f, p = divmod(t, Lf)
+            if p < S:
+                members = [f * Lf + s for s in range(S)]
+            else:
+                r, c = divmod(p - S, g.grid_w)
+                members = [f * Lf + S + rr * g.grid_w + cc for rr in range(g.grid_h)
+                           for cc in range(g.grid_w) if rr // 4 == r // 4 and cc // 4 == c // 4]
+            qb = q[members, h].mean(axis=0)
+            want = _sdpa(qb[None], kc[:, h], vc[:, h])[0]
+            _close(o[t, h], want, 1e-12)
+    rows = np.array([0, 3, 17, 40, g.n_tokens - 1])
+    _close(L.compressed_attention_pooled(q, kc, vc, g, 4, rows=rows), o[rows], 0)
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

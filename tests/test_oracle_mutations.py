@@ -52,6 +52,12 @@ MUTATIONS = [
     ("sga_mean_token_dropped", "sga_compact", "        if dropped:\n", "        if False:\n"),
     ("sga_log_count_wrong", "subsampled_attention", "math.log(len(dropped))",
      "math.log(len(dropped) + 1)"),
+    ("pooled_first_token", "compressed_attention_pooled",
+     "o_blk = dense_attention(pooled_queries(q, geom, block, blocks=need), k_cmp, v_cmp,",
+     "o_blk = dense_attention(np.stack([q[query_block_table(geom, block)[b][0]] for b in need]), k_cmp, v_cmp,"),
+    ("pooled_upsample_shifted", "compressed_attention_pooled",
+     "pos = np.searchsorted(need, owner[rows])",
+     "pos = np.minimum(np.searchsorted(need, owner[rows]) + 1, len(need) - 1)"),
     ("diag_never_added", "_subsampled_token_diagonal", "diag = was_dropped[rows % L]",
      "diag = np.zeros(len(rows), dtype=bool)"),
     ("diag_always_added", "_subsampled_token_diagonal", "diag = was_dropped[rows % L]",
