@@ -11,9 +11,10 @@ come from HIP events on that stream over the timed region.
 
 After the timed steps, variants are timed outside the step: the Speed3R GSA
 variants on the same inputs (the VGGT adaptation: reference frame 0 kept
-whole, top-16 over the other frames; the test-time top-128), the AVGGT
-subsampling factor 2..9, and AVGGT's layer schedule (frame attention for the
-early layers, subsampled after) at 100, 300 and 800 frames.
+whole, top-16 over the other frames; the test-time top-128; the block-level
+compressed branch), the AVGGT subsampling factor 2..9, its token-level
+diagonal, and AVGGT's layer schedule (frame attention for the early layers,
+subsampled after) at 100, 300 and 800 frames.
 
 Prints one JSON line. `value` = tokens of the batch / seconds per step.
 """
@@ -96,11 +97,14 @@ def main():
 
     last = {}
 
-    def gsa_chain(ev, i, top_k, keep_ref, ws_f):
+    def gsa_chain(ev, i, top_k, keep_ref, ws_f, pooled_q=False):
         """The five GSA calls, an event recorded after each."""
         k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
         ev[i].record(); i += 1
-        o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
+        if pooled_q:
+            o_cmp = sga.gsa_compressed_pooled(q32, k_cmp, v_cmp, geom)
+        else:
+            o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
         ev[i].record(); i += 1
         idx = sga.gsa_select_topk(q32, k32, geom, top_k, keep_ref=keep_ref)
         ev[i].record(); i += 1
@@ -176,7 +180,9 @@ def main():
     }
     if args.variant_steps > 0:
         layers["gsa_variants"] = {}
-        for vname, vk, vref in (("vggt_reference_frame", wl.top_k, True), ("top128", 128, False)):
+        for vname, vk, vref, vpool in (("vggt_reference_frame", wl.top_k, True, False),
+                                       ("top128", 128, False, False),
+                                       ("block_level_compressed", wl.top_k, False, True)):
             ws_v = torch.empty(sga.fine_workspace_bytes(geom, sga.SGA_BF16, True, vref),
                                dtype=torch.uint8, device=dev)
             gnames = [n for n in names if n.startswith("gsa_")]
@@ -184,17 +190,17 @@ def main():
             for rep in range(1 + args.variant_steps):  # the first pass is untimed
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(gnames) + 1)]
                 ev[0].record()
-                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v)
+                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v, vpool)
                 torch.cuda.synchronize()
                 if rep:
                     for j, n in enumerate(gnames):
                         vper[n] += ev[j].elapsed_time(ev[j + 1]) / args.variant_steps
             t_v = sum(vper.values())
             layers["gsa_variants"][vname] = {
-                "top_k": vk, "reference_frame_kept": vref, "ms": t_v,
+                "top_k": vk, "reference_frame_kept": vref, "block_level_compressed": vpool, "ms": t_v,
                 "tokens_per_s": T / t_v * 1e3, "speedup_vs_dense": per["dense"] / t_v,
                 "kernels_ms": {n[4:]: vper[n] for n in gnames},
-                "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref)}
+                "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref, pooled_q=vpool)}
             del ws_v, vidx
             print(f"[bench] variant {vname}: {t_v:.1f} ms", file=sys.stderr, flush=True)
 
@@ -306,7 +312,7 @@ def avggt_schedule(sga, torch, make_qkv, geom1000, wl, dev, timed, seed):
     return out
 
 
-def gsa_rooflines(geom, per, idx, keep_ref=False):
+def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False):
     """Per-step roofline of the GSA kernels from their timed durations:
     algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call. With
     ``keep_ref`` frame 0 is attended whole and its blocks do not compete."""
@@ -328,7 +334,7 @@ def gsa_rooflines(geom, per, idx, keep_ref=False):
     out = {}
     pool_bytes = 3 * T * H * d * 2 + N * nb * H * d * (2 + 2 + 4) + N * nqb * H * d * 4
     gate_bytes = 4 * T * H * d * 2
-    flops = {"compressed": 4.0 * T * N * nb * d * H,
+    flops = {"compressed": 4.0 * (N * nqb if pooled_q else T) * N * nb * d * H,
              "topk": 3 * 2.0 * d * (N * nqb) * n_cand * H,  # three bf16 products per score
              "fine": 4.0 * d * pairs}
     for name, nbytes in (("pool", pool_bytes), ("gate", gate_bytes)):

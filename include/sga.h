@@ -93,6 +93,23 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q,
                         float* k_cmp_f32, float* q_blk_f32, void* stream);
 
 /*
+ * GSA compressed branch at block level (Speed3R section 2.1, compression
+ * branch: the coarse results are upsampled to full resolution): the mean query
+ * of every query block (q_blk_f32 of gsa_compress) attends over the N*nb
+ * pooled keys/values, and every token of the block takes that output (nearest
+ * upsampling). The alternative to the token-level branch, where every token's
+ * own query attends (dense_global_attn with n_keys = N*nb).
+ * q_blk_f32: [N*nqb, H, d] fp32. k_cmp, v_cmp: [N*nb, H, d], o_cmp: [T, H, d],
+ * in geom->dtype.
+ * ws: sga_workspace_size(geom, SGA_OP_POOLED, 0, 0, &bytes) bytes: the
+ *   per-block outputs, and for bf16 the pooled queries in bf16 and the dense
+ *   kernel's staging.
+ */
+sga_status gsa_compressed_pooled(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                                 const void* k_cmp, const void* v_cmp, void* o_cmp, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * What the GSA selection branch always keeps (gsa_select_topk, gsa_sparse_attn):
  * SGA_KEEP_SPECIAL: every special token of every frame (the camera tokens the
  *   Speed3R VGGT adaptation keeps, Italian summary section 2; the special
@@ -187,13 +204,14 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
                                   const void* k, const void* v, void* o, void* ws,
                                   size_t ws_bytes, void* stream);
 
-enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4 };
+enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4, SGA_OP_POOLED = 5 };
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
  * stride_h, stride_w (covers every mode). SGA_OP_FINE: param0 = keep (the
  * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). SGA_OP_TOPK:
- * param0 = top_k, param1 = keep (as gsa_select_topk). */
+ * param0 = top_k, param1 = keep (as gsa_select_topk). SGA_OP_POOLED
+ * (gsa_compressed_pooled): param0 = param1 = 0. */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

@@ -22,10 +22,12 @@ SGA_OP_SUBSAMPLED = 1
 SGA_OP_DENSE = 2
 SGA_OP_FINE = 3
 SGA_OP_TOPK = 4
+SGA_OP_POOLED = 5
 SGA_KEEP_SPECIAL = 1
 SGA_KEEP_REF_FRAME = 2
 
-EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_select_topk", "gsa_sparse_attn", "gsa_gate",
+EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_compressed_pooled", "gsa_select_topk",
+           "gsa_sparse_attn", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
            "sga_version")
 
@@ -50,6 +52,7 @@ def library() -> ctypes.CDLL:
     sig = {
         "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
         "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
+        "gsa_compressed_pooled": [G, I32, P, P, P, P, P, SZ, P],
         "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
@@ -174,6 +177,33 @@ def gsa_compress(q, k, v, geom, block: int = 4, want_f32: bool = True):
     _check(library().gsa_compress(ctypes.byref(g), block, _ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp),
                                   _ptr(v_cmp), _ptr(k32), _ptr(q32), _stream(k)), "gsa_compress")
     return k_cmp, v_cmp, k32, q32
+
+
+def pooled_workspace_bytes(geom, dtype_code: int) -> int:
+    n = ctypes.c_size_t(0)
+    g = make_geom(geom, dtype_code)
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_POOLED, 0, 0, ctypes.byref(n)),
+           "sga_workspace_size")
+    return n.value
+
+
+def gsa_compressed_pooled(q_blk_f32, k_cmp, v_cmp, geom, block: int = 4, ws=None):
+    """Block-level compressed branch: each block's mean query over the pooled
+    keys, upsampled to its tokens; see include/sga.h."""
+    T, H, d, N = tokens(geom), geom.n_heads, 64, geom.n_frames
+    nb, nqb = pooled_shape(geom, block)
+    _need(q_blk_f32, "q_blk_f32", N * nqb, H, d, torch.float32)
+    _need(k_cmp, "k_cmp", N * nb, H, d)
+    _need(v_cmp, "v_cmp", N * nb, H, d, k_cmp.dtype)
+    o = torch.empty((T, H, d), dtype=k_cmp.dtype, device=k_cmp.device)
+    code = _dtype_code(k_cmp)
+    g = make_geom(geom, code)
+    ws = _workspace(pooled_workspace_bytes(geom, code), k_cmp.device, ws)
+    _check(library().gsa_compressed_pooled(ctypes.byref(g), block, _ptr(q_blk_f32), _ptr(k_cmp),
+                                           _ptr(v_cmp), _ptr(o), _ptr(ws),
+                                           0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(k_cmp)), "gsa_compressed_pooled")
+    return o
 
 
 def keep_flags(keep_special: bool = True, keep_ref: bool = False) -> int:
@@ -314,14 +344,19 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 
 
 def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
-              keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False):
+              keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False,
+              pooled_q: bool = False):
     """The Global Sparse Attention layer as its five library calls, in order:
     compress, compressed attention, select, fine attention, gate. ``keep_ref``
-    is the VGGT adaptation: frame 0 kept whole by the fine branch."""
+    is the VGGT adaptation: frame 0 kept whole by the fine branch; ``pooled_q``
+    the block-level compressed branch (pooled queries, upsampled)."""
     N = geom.n_frames
     nb, _ = pooled_shape(geom, block)
     k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block)
-    o_cmp = dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
+    if pooled_q:
+        o_cmp = gsa_compressed_pooled(q32, k_cmp, v_cmp, geom, block)
+    else:
+        o_cmp = dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
     idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q), keep_ref=keep_ref)
     o_slc = gsa_sparse_attn(q, k, v, idx, geom, top_k, keep_special, block, keep_ref=keep_ref)
     o = gsa_gate(q, o_cmp, o_slc, w_gate, b_gate, geom)

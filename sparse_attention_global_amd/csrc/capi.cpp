@@ -152,6 +152,24 @@ FineLayout fine_layout(const sga::Geom& g, bool bf, int keep) {
 }
 
 
+// gsa_compressed_pooled workspace: (bf16) the pooled queries in bf16, the
+// per-block outputs, the dense kernel's staging for the pooled keys.
+struct PooledLayout {
+  sga::Geom gq;  // the geometry seen by the dense kernel: one query per block
+  size_t q = 0, o = 0, flash = 0, total = 0;
+};
+PooledLayout pooled_layout(const sga::Geom& g, bool bf) {
+  PooledLayout lay;
+  lay.gq = g;
+  lay.gq.T = (long long)g.n_frames * g.nqb;
+  const size_t elems = (size_t)lay.gq.T * g.n_heads * sga::kHeadDim;
+  lay.q = bf ? round256(elems * 2) : 0;
+  lay.o = round256(elems * (bf ? 2 : 4));
+  lay.flash = bf ? round256(sga::flash_bf16_workspace(dense_launch(lay.gq, (long long)g.n_frames * g.nb, 0))) : 0;
+  lay.total = lay.q + lay.o + lay.flash;
+  return lay;
+}
+
 // Workspace layout of subsampled_global_attn (bf16 and fp32): compacted keys,
 // compacted values, then (bf16) the attention kernel's V^T staging.
 void subsampled_layout(const sga_geom* geom, const sga::Geom& g, int s_h, int s_w,
@@ -221,6 +239,43 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, cons
   return from_hip(sga::launch_gsa_pool(g, geom->dtype == SGA_BF16, q, k, v, k_cmp, v_cmp, k_cmp_f32,
                                        q_blk_f32, static_cast<hipStream_t>(stream)),
                   "gsa_compress launch");
+}
+
+sga_status gsa_compressed_pooled(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                                 const void* k_cmp, const void* v_cmp, void* o_cmp, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  REQUIRE_PTR(q_blk_f32);
+  REQUIRE_PTR(k_cmp);
+  REQUIRE_PTR(v_cmp);
+  REQUIRE_PTR(o_cmp);
+  const bool bf = geom->dtype == SGA_BF16;
+  const PooledLayout lay = pooled_layout(g, bf);
+  if (ws == nullptr || ws_bytes < lay.total)
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
+                ws == nullptr ? 0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  sga::FlashLaunch p = dense_launch(lay.gq, (long long)g.n_frames * g.nb, 0);
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  p.q = bf ? static_cast<const void*>(w) : static_cast<const void*>(q_blk_f32);
+  p.k = k_cmp;
+  p.v = v_cmp;
+  p.o = w + lay.q;
+  if (bf) {
+    if (sga_status st = check_fits(p)) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bf) {
+    if (hipError_t e = sga::launch_cast_bf16(q_blk_f32, w, lay.gq.T * g.n_heads * sga::kHeadDim, s))
+      return from_hip(e, "gsa_compressed_pooled (cast) launch");
+    if (hipError_t e = sga::launch_flash_bf16(p, w + lay.q + lay.o, s))
+      return from_hip(e, "gsa_compressed_pooled (attention) launch");
+  } else {
+    if (hipError_t e = sga::launch_flash_f32(p, s)) return from_hip(e, "gsa_compressed_pooled (attention) launch");
+  }
+  return from_hip(sga::launch_gsa_upsample(g, bf, w + lay.q, o_cmp, s), "gsa_compressed_pooled (upsample) launch");
 }
 
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
@@ -330,6 +385,11 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
     *bytes = geom->dtype == SGA_BF16 ? sga::flash_bf16_workspace(dense_launch(g, param0, param1)) : 0;
     return SGA_OK;
   }
+  if (op == SGA_OP_POOLED) {
+    if (param0 != 0 || param1 != 0) return fail(SGA_ERR_INVALID_ARG, "pooled workspace: param0 = param1 = 0");
+    *bytes = pooled_layout(g, geom->dtype == SGA_BF16).total;
+    return SGA_OK;
+  }
   if (op == SGA_OP_TOPK) {
     if (sga_status st = check_topk(g, param0, param1)) return st;
     *bytes = sga::gsa_topk_workspace(g, param0);
@@ -425,6 +485,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 40000; }
+int32_t sga_version(void) { return 40100; }
 
 }  // extern "C"

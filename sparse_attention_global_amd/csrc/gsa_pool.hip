@@ -81,7 +81,66 @@ __global__ __launch_bounds__(256) void gsa_pool_kernel(Geom g, const T* __restri
   if (want_q) store_f32x8(q_blk_f32 + b * rs + col, sq);
 }
 
+// bf16 copy of the fp32 pooled queries (the block-level compressed branch's
+// query operand): 8 values per thread.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const f32x4* __restrict__ x, u32x4* __restrict__ y,
+                                                       long long n8) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = x[2 * i], b = x[2 * i + 1];
+  y[i] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+               pack_bf16x2(b[2], b[3])};
+}
+
+// Nearest upsampling of per-block outputs to the tokens (Speed3R technical
+// summary section 2.1: the compressed results brought back to full
+// resolution): o[t, h] = o_blk[block(t), h], block(t) the query block of token
+// t (its 4x4 window, or its frame's special-token block). A thread per 16-byte
+// chunk; CH chunks per (token, head) row.
+template <int CH>
+__global__ __launch_bounds__(256) void upsample_kernel(Geom g, const u32x4* __restrict__ o_blk,
+                                                      u32x4* __restrict__ o) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long per_token = (long long)g.n_heads * CH;
+  if (i >= g.T * per_token) return;
+  const long long t = i / per_token, within = i % per_token;
+  const int f = (int)(t / g.L), p = (int)(t % g.L) - g.n_special;
+  long long b = (long long)f * g.nqb;
+  if (p < 0) {
+    b += g.nb;
+  } else {
+    b += (long long)((p / g.grid_w) >> 2) * g.nbw + ((p % g.grid_w) >> 2);
+  }
+  o[i] = o_blk[b * per_token + within];
+}
+
 }  // namespace
+
+hipError_t launch_cast_bf16(const float* x, void* y, long long n, hipStream_t stream) {
+  const long long n8 = n / 8;
+  const long long blocks = (n8 + 255) / 256;
+  if (n % 8 != 0 || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const f32x4*>(x), static_cast<u32x4*>(y), n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_gsa_upsample(const Geom& g, bool is_bf16, const void* o_blk, void* o,
+                               hipStream_t stream) {
+  const int ch = is_bf16 ? 8 : 16;
+  const long long n = g.T * g.n_heads * ch;
+  const long long blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (is_bf16) {
+    hipLaunchKernelGGL(upsample_kernel<8>, dim3((unsigned)blocks), dim3(256), 0, stream, g,
+                       static_cast<const u32x4*>(o_blk), static_cast<u32x4*>(o));
+  } else {
+    hipLaunchKernelGGL(upsample_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, g,
+                       static_cast<const u32x4*>(o_blk), static_cast<u32x4*>(o));
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const void* k,
                            const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,

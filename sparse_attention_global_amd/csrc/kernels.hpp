@@ -51,6 +51,12 @@ hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const voi
                            const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
                            float* q_blk_f32, hipStream_t stream);
 
+// Block-level compressed branch (gsa_pool.hip): x (n fp32, n % 8 == 0) to
+// bf16; per-block outputs [N*nqb, H, d] copied to every token of the block.
+hipError_t launch_cast_bf16(const float* x, void* y, long long n, hipStream_t stream);
+hipError_t launch_gsa_upsample(const Geom& g, bool is_bf16, const void* o_blk, void* o,
+                               hipStream_t stream);
+
 // What the GSA selection branch always keeps (the values of the C ABI's
 // SGA_KEEP_* flags): every special token; every token of reference frame 0.
 constexpr int kKeepSpecial = 1;

@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 40000
+    assert library().sga_version() == 40100
 
 
 def geom(**kw):
@@ -213,6 +213,27 @@ def test_topk_workspace():
     assert library().gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 17, 0, FAKE, None, None, 0,
                                      None) == WORKSPACE
     assert "workspace" in last_error()
+
+
+def test_pooled_workspace():
+    g = geom(n_frames=256)
+    nq = 256 * 101
+    # bf16: the pooled queries in bf16, the per-block outputs, and the dense
+    # staging over the 25,600 pooled keys (V^T, key-norm partials, one redo flag
+    # per 128-query workgroup)
+    blk = r256(nq * 16 * 64 * 2)
+    flash = r256(16 * 64 * 25600 * 2 + 16 * 256 * 4 + r256(-(-nq // 128) * 16))
+    assert _ws(g, 5, 0, 0) == (OK, 2 * blk + flash)
+    # fp32: the per-block outputs only
+    assert _ws(geom(n_frames=3, dtype=1), 5, 0, 0) == (OK, r256(3 * 101 * 16 * 64 * 4))
+    assert _ws(g, 5, 1, 0)[0] == INVALID
+    L = library()
+    assert L.gsa_compressed_pooled(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, None, 0, None) == WORKSPACE
+    assert "workspace" in last_error()
+    assert L.gsa_compressed_pooled(ctypes.byref(g), 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                   None) == UNSUPPORTED
+    assert L.gsa_compressed_pooled(ctypes.byref(g), 4, None, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                   None) == INVALID
 
 
 def test_python_layer_requires_gpu_tensors():

@@ -426,6 +426,37 @@ def test_subsampled_token_diagonal(geom, stride):
         assert_close(host(o), oracle.dense_attention(qh, kh, vh), geom.dtype, "token diagonal stride 1")
 
 
+@pytest.mark.parametrize("geom,top_k", [
+    pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), 5, id="ragged-bf16"),
+    pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), 3, id="ragged-f32"),
+    pytest.param(Geometry(6, 5, 37, 37, 2, 64, "bf16"), 16, id="scene-bf16"),
+    pytest.param(Geometry(2, 0, 8, 8, 2, 64, "bf16"), 4, id="no-specials-bf16"),
+])
+def test_compressed_pooled(geom, top_k):
+    """The block-level compressed branch: every row against the oracle (the
+    oracle's own pooling and block means), and the whole layer on decided rows."""
+    _announce(f"compressed branch at block level {geom}")
+    dist = "normal" if geom.dtype == "f32" else "scene"
+    q, k, v = make_qkv(geom, seed=81, device=DEV, distribution=dist)
+    w, b = make_gate(geom.n_heads, 64, seed=81, device=DEV)
+    k_cmp, v_cmp, _, q32 = sga.gsa_compress(q, k, v, geom)
+    o = sga.gsa_compressed_pooled(q32, k_cmp, v_cmp, geom)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    rkc, rvc = oracle.compress(kh, vh, geom, 4)
+    assert_close(host(o), oracle.compressed_attention_pooled(qh, rkc, rvc, geom, 4), geom.dtype,
+                 "o_cmp (block level)")
+    out = sga.gsa_layer(q, k, v, w, b, geom, top_k, pooled_q=True)
+    _sync()
+    ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), top_k, pooled_q=True)
+    dec = decided_blocks(ref["ranked"], top_k).all(axis=0)
+    owner = _owner_blocks(geom, np.arange(geom.n_tokens))
+    pos = {bb: i for i, bb in enumerate(ref["blocks"])}
+    rows = np.array([t for t in range(geom.n_tokens) if dec[pos[owner[t]]]])
+    assert len(rows) >= 64
+    assert_close(host(out)[rows], ref["o"][rows], geom.dtype, "gsa layer (block-level compressed)")
+
+
 def test_deterministic():
     geom = Geometry(8, 5, 37, 37, 4, 64, "bf16")
     _announce(f"determinism {geom}")
@@ -500,17 +531,19 @@ def _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, top_k, name, keep_
     assert_close(host(o)[rows], ref["o"], "bf16", f"{name} gsa layer (oracle sets, all rows)")
 
 
-def _gsa_check(name, rows_cap=None, keep_ref=False):
+def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False):
     wl, geom, q, k, v = _workload_inputs(name)
     w, b = make_gate(geom.n_heads, 64, seed=1, device=DEV)
     rows = sample_rows(geom.n_tokens, rows_cap or wl.check_rows, seed=1).numpy()
-    _announce(f"{name} GSA layer (reference frame kept: {keep_ref}), {len(rows)} rows")
-    out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True, keep_ref=keep_ref)
+    _announce(f"{name} GSA layer (reference frame kept: {keep_ref}, block-level compressed: "
+              f"{pooled_q}), {len(rows)} rows")
+    out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True, keep_ref=keep_ref,
+                        pooled_q=pooled_q)
     _sync()
     qh, kh, vh = host(q), host(k), host(v)
     W = oracle_workers()
     ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), wl.top_k, rows=rows, workers=W,
-                           keep_ref=keep_ref)
+                           keep_ref=keep_ref, pooled_q=pooled_q)
     assert_close(host(out["k_cmp"]), ref["k_cmp"], "bf16", f"{name} k_cmp")
     assert_close(host(out["v_cmp"]), ref["v_cmp"], "bf16", f"{name} v_cmp")
     assert_close(host(out["k_cmp_f32"]), ref["k_cmp"], "f32", f"{name} k_cmp_f32")
@@ -538,6 +571,11 @@ def test_gsa128():
 @pytest.mark.timeout(900)
 def test_gsa128_reference_frame():
     _gsa_check("gsa128", rows_cap=1024, keep_ref=True)
+
+
+@pytest.mark.timeout(900)
+def test_gsa128_block_level_compressed():
+    _gsa_check("gsa128", rows_cap=1024, pooled_q=True)
 
 
 def _sga_check(name, rows_cap=None):
