@@ -677,3 +677,47 @@ def test_scene1000_subsampled(scene1000):
     assert_close(host(o)[rows], np.concatenate(ref), "bf16", "scene1000 subsampled")
     assert_close(host(of)[rows], oracle.frame_attention(qh, kh, vh, geom, rows=rows), "bf16",
                  "scene1000 frame")
+
+
+@pytest.mark.timeout(1200)
+def test_scene1000_variants(scene1000):
+    """The variants the benchmark times at 1000 frames, on 512 sampled rows:
+    top-128 selection, the VGGT reference frame (selection and fine branch),
+    the block-level compressed branch and the token-level AVGGT diagonal."""
+    wl, geom, q, k, v, probes, (qh, kh, vh) = scene1000
+    rows = sample_rows(geom.n_tokens, 512, seed=9).numpy()
+    nb = _nb(geom)
+    W = oracle_workers()
+    _announce(f"scene1000 variants, {len(rows)} rows")
+    k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
+    idx128 = sga.gsa_select_topk(q32, k32, geom, 128)
+    idx_ref = sga.gsa_select_topk(q32, k32, geom, wl.top_k, keep_ref=True)
+    o_blk = sga.gsa_compressed_pooled(q32, k_cmp, v_cmp, geom)
+    o_diag = sga.subsampled_global_attn(q, k, v, geom, *wl.stride, mode=2)
+    _sync()
+    rkc, rvc = oracle.compress(kh, vh, geom, 4)
+    print("[oracle] scene1000 pooled keys ready", flush=True)
+    need = np.unique(_owner_blocks(geom, rows))
+    rqb = oracle.pooled_queries(qh, geom, 4, blocks=need)
+    ridx, ranked = oracle.select_topk(rqb, rkc, 128, workers=W)
+    check_topk(host(idx128).astype(np.int64)[:, need], ridx, ranked, rqb, rkc, "scene1000 top-128")
+    ridx_r, ranked_r = oracle.select_topk(rqb, rkc, wl.top_k, workers=W, first=nb)
+    check_topk(host(idx_ref).astype(np.int64)[:, need], ridx_r, ranked_r, rqb, rkc,
+               "scene1000 top-K (reference frame kept)")
+    # the fine branch with frame 0 kept whole, fed the oracle's index sets
+    idx_mix = idx_ref.clone()
+    idx_mix[:, torch.from_numpy(need).to(DEV)] = torch.from_numpy(ridx_r).to(DEV)
+    o_slc = sga.gsa_sparse_attn(q, k, v, idx_mix, geom, wl.top_k, keep_ref=True)
+    _sync()
+    idx_full = np.zeros((geom.n_heads, geom.n_frames * _nqb(geom), wl.top_k), dtype=np.int32)
+    idx_full[:, need] = ridx_r
+    assert_close(host(o_slc)[rows], oracle.fine_attention(qh, kh, vh, geom, 4, idx_full, rows=rows,
+                                                          keep_ref=True, workers=W),
+                 "bf16", "scene1000 o_slc (reference frame kept)")
+    assert_close(host(o_blk)[rows], oracle.compressed_attention_pooled(qh, rkc, rvc, geom, 4,
+                                                                      rows=rows, workers=W),
+                 "bf16", "scene1000 o_cmp (block level)")
+    sh, sw = wl.stride
+    assert_close(host(o_diag)[rows], oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, mode=2,
+                                                                 rows=rows, workers=W),
+                 "bf16", "scene1000 subsampled token diagonal")
