@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="scene1000")
-    ap.add_argument("--cpu-rows", type=int, default=128,
+    ap.add_argument("--cpu-rows", type=int, default=384,
                     help="query rows of the CPU-oracle baseline sample (0 disables it)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--variant-steps", type=int, default=1,
