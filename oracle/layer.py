@@ -53,7 +53,11 @@ R17 AVGGT's "diagonal" read at token level (the alternative to R9, mode 2):
     its patch was dropped; the means stay per frame, over all dropped patches;
 R18 the compressed branch read at block level (the alternative to R1): each
     query block's mean query attends over the pooled keys/values and every
-    token of the block takes that output (nearest upsampling).
+    token of the block takes that output (nearest upsampling);
+R19 the grid zero-padded to whole windows before the 4x4 average (the
+    alternative to R4): a window that overhangs the grid sums its in-grid
+    tokens and divides by 16. The mean queries of the query blocks (R2, R3)
+    stay over their tokens.
 
 Arrays are ``[rows, H, d]`` of any float dtype; every computation widens them
 to fp64 first.
@@ -240,18 +244,21 @@ class _one_frame:
         self.grid_h, self.grid_w = geom.grid_h, geom.grid_w
 
 
-def compress(k, v, geom, block: int = 4):
+def compress(k, v, geom, block: int = 4, include_pad: bool = False):
     """4x4 average pooling of keys and values into the coarse context
     ([Speed3R-ja] section 2.1, compression branch, first bullet;
     [Speed3R-it] section 2, "Ramo di Compressione"). Mean over the valid
-    tokens of each window (R4). Returns fp64 (k_cmp, v_cmp) [N*nb, H, d]."""
+    tokens of each window (R4); with ``include_pad`` the grid is zero-padded to
+    whole windows and every window is divided by block^2 (R19).
+    Returns fp64 (k_cmp, v_cmp) [N*nb, H, d]."""
     win = window_table(geom, block)
     H, d = k.shape[1], k.shape[2]
     kc = np.empty((len(win), H, d))
     vc = np.empty((len(win), H, d))
     for j, rows in enumerate(win):
-        kc[j] = np.asarray(k[rows], dtype=np.float64).mean(axis=0)
-        vc[j] = np.asarray(v[rows], dtype=np.float64).mean(axis=0)
+        den = block * block if include_pad else len(rows)
+        kc[j] = np.asarray(k[rows], dtype=np.float64).sum(axis=0) / den
+        vc[j] = np.asarray(v[rows], dtype=np.float64).sum(axis=0) / den
     return kc, vc
 
 
@@ -410,14 +417,16 @@ def gate(q, o_cmp, o_slc, w, b):
 
 
 def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
-              keep_special=True, workers=None, keep_ref=False, pooled_q=False):
+              keep_special=True, workers=None, keep_ref=False, pooled_q=False,
+              include_pad=False):
     """The whole Global Sparse Attention layer for the query rows ``rows``:
     pool, compressed branch, block scores + top-K, fine branch, gate.
     ``keep_ref`` is the VGGT adaptation (R15); ``pooled_q`` the block-level
-    compressed branch (R18). Returns a dict with every intermediate."""
+    compressed branch (R18); ``include_pad`` the zero-padded pooling (R19).
+    Returns a dict with every intermediate."""
     T = q.shape[0]
     rows = _rows(rows, T)
-    k_cmp, v_cmp = compress(k, v, geom, block)
+    k_cmp, v_cmp = compress(k, v, geom, block, include_pad=include_pad)
     if pooled_q:
         o_cmp = compressed_attention_pooled(q, k_cmp, v_cmp, geom, block, rows=rows, workers=workers)
     else:

@@ -601,4 +601,26 @@ def pin_pooled_compressed_vs_sdpa():
     rows = np.array([0, 3, 17, 40, g.n_tokens - 1])
     _close(L.compressed_attention_pooled(q, kc, vc, g, 4, rows=rows), o[rows], 0)
 
+
+def pin_pool_zero_padded():
+    """Zero-padded pooling (R19) equals numpy: the grid padded with zeros to
+    whole 4x4 windows, reshaped into windows and averaged over all 16 slots;
+    on a grid of whole windows it equals the valid-token mean (R4)."""
+    g = G_SMALL
+    q, k, v = _qkv(g, 30)
+    kc, vc = L.compress(k, v, g, 4, include_pad=True)
+    Lf, S = g.tokens_per_frame, g.n_special
+    nbh, nbw = -(-g.grid_h // 4), -(-g.grid_w // 4)
+    for f in range(g.n_frames):
+        for x, xc in ((k, kc), (v, vc)):
+            grid = x[f * Lf + S:(f + 1) * Lf].reshape(g.grid_h, g.grid_w, g.n_heads, g.head_dim)
+            pad = np.zeros((4 * nbh, 4 * nbw, g.n_heads, g.head_dim))
+            pad[:g.grid_h, :g.grid_w] = grid
+            want = pad.reshape(nbh, 4, nbw, 4, g.n_heads, g.head_dim).mean(axis=(1, 3))
+            _close(xc[f * nbh * nbw:(f + 1) * nbh * nbw], want.reshape(-1, g.n_heads, g.head_dim),
+                   1e-14)
+    q, k, v = _qkv(G_FULL, 31)
+    for a, b in zip(L.compress(k, v, G_FULL, 4, include_pad=True), L.compress(k, v, G_FULL, 4)):
+        _close(a, b, 1e-15)
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

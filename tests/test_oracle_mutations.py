@@ -23,9 +23,6 @@ MUTATIONS = [
     ("window_no_clip_rows", "window_table", "min(block * by + block, gh)", "block * by + block"),
     ("window_transposed", "window_table", "rows.append(f * L + S + r * gw + c)",
      "rows.append(f * L + S + c * gh + r)"),
-    ("pool_counts_padding", "compress",
-     "kc[j] = np.asarray(k[rows], dtype=np.float64).mean(axis=0)",
-     "kc[j] = np.asarray(k[rows], dtype=np.float64).sum(axis=0) / block ** 2"),
     ("no_special_query_block", "query_block_table", "        if S:\n", "        if False:\n"),
     ("block_score_unscaled", "block_scores", "/ math.sqrt(d)", ""),
     ("topk_ties_high", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (-row[j], -j)"),
@@ -52,6 +49,9 @@ MUTATIONS = [
     ("sga_mean_token_dropped", "sga_compact", "        if dropped:\n", "        if False:\n"),
     ("sga_log_count_wrong", "subsampled_attention", "math.log(len(dropped))",
      "math.log(len(dropped) + 1)"),
+    ("pad_ignored", "compress", "den = block * block if include_pad else len(rows)", "den = len(rows)"),
+    ("pad_divides_valid_by_16", "compress", "den = block * block if include_pad else len(rows)",
+     "den = block * block"),
     ("pooled_first_token", "compressed_attention_pooled",
      "o_blk = dense_attention(pooled_queries(q, geom, block, blocks=need), k_cmp, v_cmp,",
      "o_blk = dense_attention(np.stack([q[query_block_table(geom, block)[b][0]] for b in need]), k_cmp, v_cmp,"),
