@@ -12,7 +12,7 @@ come from HIP events on that stream over the timed region.
 After the timed steps, variants are timed outside the step: the Speed3R GSA
 variants on the same inputs (the VGGT adaptation: reference frame 0 kept
 whole, top-16 over the other frames; the test-time top-128; the block-level
-compressed branch), the AVGGT subsampling factor 2..9, its token-level
+compressed branch; pooling of the zero-padded grid), the AVGGT subsampling factor 2..9, its token-level
 diagonal, and AVGGT's layer schedule (frame attention for the early layers,
 subsampled after) at 100, 300 and 800 frames.
 
@@ -97,9 +97,9 @@ def main():
 
     last = {}
 
-    def gsa_chain(ev, i, top_k, keep_ref, ws_f, pooled_q=False):
+    def gsa_chain(ev, i, top_k, keep_ref, ws_f, pooled_q=False, include_pad=False):
         """The five GSA calls, an event recorded after each."""
-        k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom)
+        k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom, include_pad=include_pad)
         ev[i].record(); i += 1
         if pooled_q:
             o_cmp = sga.gsa_compressed_pooled(q32, k_cmp, v_cmp, geom)
@@ -159,7 +159,6 @@ def main():
     keys_sga = geom.tokens_per_frame + (N - 1) * (mk + has_mean)
     flop_sga = 4.0 * T * keys_sga * d * H
     t_gsa = sum(per[n] for n in names if n.startswith("gsa_"))
-    gsa_roof = gsa_rooflines(geom, per, last["idx"])
     layers = {
         "dense": {"ms": per["dense"], "tokens_per_s": T / per["dense"] * 1e3,
                   "tflops": flop_dense / per["dense"] / 1e9,
@@ -172,7 +171,7 @@ def main():
                 "kernels_ms": {n[4:]: per[n] for n in names if n.startswith("gsa_")},
                 "compressed_tflops": flop_cmp / per["gsa_compressed"] / 1e9,
                 "compressed_mfma_frac": flop_cmp / per["gsa_compressed"] / 1e9 / PEAK_BF16_TFLOPS,
-                "kernels_roofline": gsa_roof},
+                "kernels_roofline": None},
         "subsampled": {"ms": per["sga"], "tokens_per_s": T / per["sga"] * 1e3,
                        "speedup_vs_dense": per["dense"] / per["sga"],
                        "tflops": flop_sga / per["sga"] / 1e9,
@@ -180,9 +179,10 @@ def main():
     }
     if args.variant_steps > 0:
         layers["gsa_variants"] = {}
-        for vname, vk, vref, vpool in (("vggt_reference_frame", wl.top_k, True, False),
-                                       ("top128", 128, False, False),
-                                       ("block_level_compressed", wl.top_k, False, True)):
+        for vname, vk, vref, vpool, vpad in (("vggt_reference_frame", wl.top_k, True, False, False),
+                                             ("top128", 128, False, False, False),
+                                             ("block_level_compressed", wl.top_k, False, True, False),
+                                             ("zero_padded_pooling", wl.top_k, False, False, True)):
             ws_v = torch.empty(sga.fine_workspace_bytes(geom, sga.SGA_BF16, True, vref),
                                dtype=torch.uint8, device=dev)
             gnames = [n for n in names if n.startswith("gsa_")]
@@ -190,20 +190,22 @@ def main():
             for rep in range(1 + args.variant_steps):  # the first pass is untimed
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(gnames) + 1)]
                 ev[0].record()
-                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v, vpool)
+                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v, vpool, vpad)
                 torch.cuda.synchronize()
                 if rep:
                     for j, n in enumerate(gnames):
                         vper[n] += ev[j].elapsed_time(ev[j + 1]) / args.variant_steps
             t_v = sum(vper.values())
             layers["gsa_variants"][vname] = {
-                "top_k": vk, "reference_frame_kept": vref, "block_level_compressed": vpool, "ms": t_v,
+                "top_k": vk, "reference_frame_kept": vref, "block_level_compressed": vpool,
+                "zero_padded_pooling": vpad, "ms": t_v,
                 "tokens_per_s": T / t_v * 1e3, "speedup_vs_dense": per["dense"] / t_v,
                 "kernels_ms": {n[4:]: vper[n] for n in gnames},
                 "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref, pooled_q=vpool)}
             del ws_v, vidx
             print(f"[bench] variant {vname}: {t_v:.1f} ms", file=sys.stderr, flush=True)
 
+    fine_windows_ms = None
     if args.variant_steps > 0:
         def timed(fn, reps):
             """ms per call from HIP events on the current stream; one untimed call first."""
@@ -218,6 +220,15 @@ def main():
                 t += e0.elapsed_time(e1) / reps
             return t
 
+        # the fine branch's window kernel alone (no always-kept tokens)
+        fine_windows_ms = timed(lambda: sga.gsa_sparse_attn(q, k, v, last["idx"], geom, wl.top_k,
+                                                            keep_special=False), args.variant_steps)
+        # AVGGT compaction alone (HBM: read K and V, write the compacted set)
+        t_cp = timed(lambda: sga.sga_compact(k, v, geom, sh, sw), args.variant_steps)
+        cp_bytes = 2 * T * H * d * 2 + 2 * N * (mk + has_mean) * H * d * 2
+        layers["subsampled"]["compaction"] = {
+            "ms": t_cp, "bound": "hbm", "gb_per_s": cp_bytes / (t_cp * 1e-3) / 1e9,
+            "frac": cp_bytes / (t_cp * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": cp_bytes}
         # AVGGT subsampling factor sigma = 2..9 (sigma x sigma windows)
         sweep = {}
         for sig in range(2, 10):
@@ -248,6 +259,9 @@ def main():
               file=sys.stderr, flush=True)
         layers["avggt_schedule"] = avggt_schedule(sga, torch, make_qkv, geom, wl, dev, timed,
                                                   args.seed)
+
+    layers["gsa"]["kernels_roofline"] = gsa_rooflines(geom, per, last["idx"],
+                                                      fine_windows_ms=fine_windows_ms)
 
     achieved = flop_dense / (per["dense"] * 1e-3) / 1e12
     roofline = {"kernel": "flash_bf16_kernel<GLOBAL> (dense global attention)",
@@ -312,10 +326,13 @@ def avggt_schedule(sga, torch, make_qkv, geom1000, wl, dev, timed, seed):
     return out
 
 
-def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False):
+def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False, fine_windows_ms=None):
     """Per-step roofline of the GSA kernels from their timed durations:
     algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call. With
-    ``keep_ref`` frame 0 is attended whole and its blocks do not compete."""
+    ``keep_ref`` frame 0 is attended whole and its blocks do not compete.
+    Given the time of the fine branch's window kernel alone, the fine branch is
+    split into its window gather (bytes of the selected keys and values) and
+    the attention over the always-kept tokens (MFMA)."""
     import torch
     T, H, d, N, S = geom.n_tokens, geom.n_heads, geom.head_dim, geom.n_frames, geom.n_special
     nbh, nbw = -(-geom.grid_h // 4), -(-geom.grid_w // 4)
@@ -330,12 +347,13 @@ def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False):
     per_block = qcount.repeat(N)[None, :].double()            # queries per block
     kept = (geom.tokens_per_frame + (N - 1) * S) if keep_ref else N * S
     pairs = float((per_block * (sel.double() + kept)).sum())  # (query, key) pairs, all heads
+    kept_pairs = float(per_block.sum()) * H * kept
     n_cand = (N - 1) * nb if keep_ref else N * nb
     out = {}
     pool_bytes = 3 * T * H * d * 2 + N * nb * H * d * (2 + 2 + 4) + N * nqb * H * d * 4
     gate_bytes = 4 * T * H * d * 2
     flops = {"compressed": 4.0 * (N * nqb if pooled_q else T) * N * nb * d * H,
-             "topk": 3 * 2.0 * d * (N * nqb) * n_cand * H,  # three bf16 products per score
+             "topk": 2.0 * d * (N * nqb) * n_cand * H,  # one product per score
              "fine": 4.0 * d * pairs}
     for name, nbytes in (("pool", pool_bytes), ("gate", gate_bytes)):
         gbs = nbytes / (per["gsa_" + name] * 1e-3) / 1e9
@@ -343,6 +361,21 @@ def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False):
     for name, fl in flops.items():
         tf = fl / (per["gsa_" + name] * 1e-3) / 1e12
         out[name] = {"bound": "mfma", "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS, "flop": fl}
+    # the scores run as three bf16 products (hi*hi + hi*lo + lo*hi) for fp32 accuracy
+    out["topk"]["executed_flop"] = 3 * flops["topk"]
+    out["topk"]["executed_tflops"] = 3 * out["topk"]["tflops"]
+    # in-grid tokens per selected window (16 for an inner window, 4 or 1 at the edges)
+    out["fine"]["selected_tokens_per_window"] = float(sel.double().sum()) / idx.numel()
+    if fine_windows_ms is not None:
+        gather_bytes = float(sel.double().sum()) * d * 2 * 2   # selected keys' K and V rows, bf16
+        gbs = gather_bytes / (fine_windows_ms * 1e-3) / 1e9
+        out["fine_windows"] = {"bound": "gather (HBM/L2)", "ms": fine_windows_ms, "gb_per_s": gbs,
+                               "frac": gbs / PEAK_HBM_GBS, "bytes": gather_bytes}
+        t_kept = per["gsa_fine"] - fine_windows_ms
+        if t_kept > 0:
+            tf = 4.0 * d * kept_pairs / (t_kept * 1e-3) / 1e12
+            out["fine_kept"] = {"bound": "mfma", "ms": t_kept, "tflops": tf,
+                                "frac": tf / PEAK_BF16_TFLOPS, "flop": 4.0 * d * kept_pairs}
     return out
 
 
@@ -399,7 +432,10 @@ def cpu_baseline(q, k, v, w, b, geom, wl, n_rows, seed):
                       f"forms (dense, frame, GSA incl. its full pooling, subsampled incl. its full "
                       f"compaction), fp64 NumPy oracle; {total:.1f} s",
             "seconds": {"dense": t1 - t0, "frame": t2 - t1, "gsa": t3 - t2,
-                        "subsampled": t4 - t3}}
+                        "subsampled": t4 - t3},
+            # the whole layer step at this rate (the pooling and compaction of the
+            # sample are whole-batch already, so this overstates them)
+            "extrapolated_full_step_s": total * geom.n_tokens / len(rows)}
 
 
 if __name__ == "__main__":

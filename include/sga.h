@@ -77,7 +77,10 @@ sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
 /*
  * GSA compression (Speed3R section 2.1, compression branch): block x block
  * average pooling of K and V over the patch grid, averaging only the tokens
- * that fall inside the grid. Only block == 4 is supported.
+ * that fall inside the grid (include_pad == 0), or with the grid zero-padded
+ * to whole windows (include_pad == 1: the in-grid sum over block^2; the
+ * configuration's "37x37 padded to 40x40" read literally). Only block == 4 is
+ * supported. The mean queries are over each block's tokens either way.
  *   nbh = ceil(grid_h/4), nbw = ceil(grid_w/4), nb = nbh*nbw,
  *   nqb = nb + (n_special > 0 ? 1 : 0).
  * Pooled key j = f*nb + by*nbw + bx covers patch rows 4by..4by+3 and columns
@@ -88,9 +91,9 @@ sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
  *   block: the windows of a frame in pooled-key order, then one block holding
  *   the frame's special tokens.
  */
-sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q,
-                        const void* k, const void* v, void* k_cmp, void* v_cmp,
-                        float* k_cmp_f32, float* q_blk_f32, void* stream);
+sga_status gsa_compress(const sga_geom* geom, int32_t block, int32_t include_pad,
+                        const void* q, const void* k, const void* v, void* k_cmp,
+                        void* v_cmp, float* k_cmp_f32, float* q_blk_f32, void* stream);
 
 /*
  * GSA compressed branch at block level (Speed3R section 2.1, compression

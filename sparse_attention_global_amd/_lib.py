@@ -51,7 +51,7 @@ def library() -> ctypes.CDLL:
     G = ctypes.POINTER(SgaGeom)
     sig = {
         "dense_global_attn": [G, P, P, P, I64, I32, P, P, P, SZ, P],
-        "gsa_compress": [G, I32, P, P, P, P, P, P, P, P],
+        "gsa_compress": [G, I32, I32, P, P, P, P, P, P, P, P],
         "gsa_compressed_pooled": [G, I32, P, P, P, P, P, SZ, P],
         "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
@@ -159,8 +159,9 @@ def dense_global_attn(q, k, v, geom, n_keys: int = 0, frame_local: bool = False,
     return (o, lse) if want_lse else o
 
 
-def gsa_compress(q, k, v, geom, block: int = 4, want_f32: bool = True):
-    """Pooled K/V (+ fp32 pooled K and pooled queries); see include/sga.h."""
+def gsa_compress(q, k, v, geom, block: int = 4, want_f32: bool = True, include_pad: bool = False):
+    """Pooled K/V (+ fp32 pooled K and pooled queries); ``include_pad`` pools
+    the zero-padded grid; see include/sga.h."""
     T, H, d = tokens(geom), geom.n_heads, 64
     nb, nqb = pooled_shape(geom, block)
     _need(k, "k", T, H, d)
@@ -174,7 +175,8 @@ def gsa_compress(q, k, v, geom, block: int = 4, want_f32: bool = True):
     q32 = (torch.empty((N * nqb, H, d), dtype=torch.float32, device=k.device)
            if (want_f32 and q is not None) else None)
     g = make_geom(geom, _dtype_code(k))
-    _check(library().gsa_compress(ctypes.byref(g), block, _ptr(q), _ptr(k), _ptr(v), _ptr(k_cmp),
+    _check(library().gsa_compress(ctypes.byref(g), block, int(include_pad), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(k_cmp),
                                   _ptr(v_cmp), _ptr(k32), _ptr(q32), _stream(k)), "gsa_compress")
     return k_cmp, v_cmp, k32, q32
 
@@ -345,14 +347,15 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 
 def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
               keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False,
-              pooled_q: bool = False):
+              pooled_q: bool = False, include_pad: bool = False):
     """The Global Sparse Attention layer as its five library calls, in order:
     compress, compressed attention, select, fine attention, gate. ``keep_ref``
     is the VGGT adaptation: frame 0 kept whole by the fine branch; ``pooled_q``
-    the block-level compressed branch (pooled queries, upsampled)."""
+    the block-level compressed branch (pooled queries, upsampled);
+    ``include_pad`` the zero-padded pooling."""
     N = geom.n_frames
     nb, _ = pooled_shape(geom, block)
-    k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block)
+    k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block, include_pad=include_pad)
     if pooled_q:
         o_cmp = gsa_compressed_pooled(q32, k_cmp, v_cmp, geom, block)
     else:

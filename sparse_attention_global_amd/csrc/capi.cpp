@@ -223,12 +223,13 @@ sga_status dense_global_attn(const sga_geom* geom, const void* q, const void* k,
   return from_hip(sga::launch_flash_bf16(p, ws, s), "dense_global_attn launch");
 }
 
-sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, const void* k,
-                        const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
+sga_status gsa_compress(const sga_geom* geom, int32_t block, int32_t include_pad, const void* q,
+                        const void* k, const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
                         float* q_blk_f32, void* stream) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
+  if (include_pad != 0 && include_pad != 1) return fail(SGA_ERR_INVALID_ARG, "include_pad must be 0 or 1");
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(k_cmp);
@@ -236,7 +237,7 @@ sga_status gsa_compress(const sga_geom* geom, int32_t block, const void* q, cons
   REQUIRE_OPT_PTR(k_cmp_f32);
   REQUIRE_OPT_PTR(q_blk_f32);
   if (q_blk_f32 != nullptr) REQUIRE_PTR(q);
-  return from_hip(sga::launch_gsa_pool(g, geom->dtype == SGA_BF16, q, k, v, k_cmp, v_cmp, k_cmp_f32,
+  return from_hip(sga::launch_gsa_pool(g, geom->dtype == SGA_BF16, include_pad, q, k, v, k_cmp, v_cmp, k_cmp_f32,
                                        q_blk_f32, static_cast<hipStream_t>(stream)),
                   "gsa_compress launch");
 }
@@ -485,6 +486,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 40100; }
+int32_t sga_version(void) { return 50000; }
 
 }  // extern "C"

@@ -3,8 +3,10 @@
 // context, plus the mean query of every query block (the pooled query whose
 // logit against a pooled key is the block score used for selection).
 //
-// Windows that overhang the grid average only their in-grid tokens. Special
-// tokens are never pooled into K/V; they form one extra query block per frame.
+// Windows that overhang the grid average only their in-grid tokens, or, with
+// include_pad, the grid counts as zero-padded to whole windows (the in-grid
+// sum over 16). Special tokens are never pooled into K/V; they form one extra
+// query block per frame. The mean queries are always over the block's tokens.
 //
 // Work split: one thread per (query block, head, 8-element chunk of d); eight
 // consecutive threads cover one 128-byte head row and the heads of a token are
@@ -21,7 +23,7 @@ __global__ __launch_bounds__(256) void gsa_pool_kernel(Geom g, const T* __restri
                                                        const T* __restrict__ k,
                                                        const T* __restrict__ v, T* k_cmp,
                                                        T* v_cmp, float* k_cmp_f32,
-                                                       float* q_blk_f32) {
+                                                       float* q_blk_f32, int include_pad) {
   const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int chunk = (int)(tid & 7);
   const int h = (int)((tid >> 3) % g.n_heads);
@@ -72,8 +74,9 @@ __global__ __launch_bounds__(256) void gsa_pool_kernel(Geom g, const T* __restri
     }
   }
   const float inv = 1.f / (float)((r1 - r0) * (c1 - c0));
+  const float inv_kv = include_pad ? 1.f / 16.f : inv;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) { sk[e] *= inv; sv[e] *= inv; sq[e] *= inv; }
+  for (int e = 0; e < 8; ++e) { sk[e] *= inv_kv; sv[e] *= inv_kv; sq[e] *= inv; }
   const long long kj = (long long)f * g.nb + j;
   Chunk8<T>::store(k_cmp + kj * rs + col, sk);
   Chunk8<T>::store(v_cmp + kj * rs + col, sv);
@@ -142,9 +145,9 @@ hipError_t launch_gsa_upsample(const Geom& g, bool is_bf16, const void* o_blk, v
   return hipGetLastError();
 }
 
-hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const void* k,
-                           const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
-                           float* q_blk_f32, hipStream_t stream) {
+hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, int include_pad, const void* q,
+                           const void* k, const void* v, void* k_cmp, void* v_cmp,
+                           float* k_cmp_f32, float* q_blk_f32, hipStream_t stream) {
   const long long threads = (long long)g.n_frames * g.nqb * g.n_heads * 8;
   const long long blocks = (threads + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -152,12 +155,12 @@ hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const voi
     hipLaunchKernelGGL(gsa_pool_kernel<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream, g,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                        static_cast<const bf16*>(v), static_cast<bf16*>(k_cmp),
-                       static_cast<bf16*>(v_cmp), k_cmp_f32, q_blk_f32);
+                       static_cast<bf16*>(v_cmp), k_cmp_f32, q_blk_f32, include_pad);
   } else {
     hipLaunchKernelGGL(gsa_pool_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream, g,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), static_cast<float*>(k_cmp),
-                       static_cast<float*>(v_cmp), k_cmp_f32, q_blk_f32);
+                       static_cast<float*>(v_cmp), k_cmp_f32, q_blk_f32, include_pad);
   }
   return hipGetLastError();
 }

@@ -47,9 +47,9 @@ hipError_t launch_vt_prepare(const void* v, int n_heads, long long n_rows, long 
 hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream);
 
 // GSA pooling (gsa_pool.hip). is_bf16 selects the I/O dtype.
-hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, const void* q, const void* k,
-                           const void* v, void* k_cmp, void* v_cmp, float* k_cmp_f32,
-                           float* q_blk_f32, hipStream_t stream);
+hipError_t launch_gsa_pool(const Geom& g, bool is_bf16, int include_pad, const void* q,
+                           const void* k, const void* v, void* k_cmp, void* v_cmp,
+                           float* k_cmp_f32, float* q_blk_f32, hipStream_t stream);
 
 // Block-level compressed branch (gsa_pool.hip): x (n fp32, n % 8 == 0) to
 // bf16; per-block outputs [N*nqb, H, d] copied to every token of the block.

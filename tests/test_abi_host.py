@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 40100
+    assert library().sga_version() == 50000
 
 
 def geom(**kw):
@@ -83,10 +83,12 @@ def test_dense_rejects_null_and_misaligned():
 def test_gsa_calls_reject_bad_arguments():
     L = library()
     g = geom()
-    assert L.gsa_compress(ctypes.byref(g), 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == UNSUPPORTED
+    assert L.gsa_compress(ctypes.byref(g), 2, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == UNSUPPORTED
     assert "block" in last_error()
     # pooled queries requested without q
-    assert L.gsa_compress(ctypes.byref(g), 4, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert L.gsa_compress(ctypes.byref(g), 4, 0, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    assert L.gsa_compress(ctypes.byref(g), 4, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INVALID
+    assert "include_pad" in last_error()
     nb = 2 * 100
     for bad_k in (0, nb + 1, 129):
         assert L.gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, bad_k, 0, FAKE, None, None, 0, None) == INVALID
