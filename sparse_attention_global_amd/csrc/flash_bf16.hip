@@ -195,8 +195,10 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
   }
   seg1 = Segment{A.ck, 0, A.cvt, 0, A.cvt_ld,
                  MODE == MODE_SUBSAMPLED ? (long long)A.g.n_frames * (A.mk + A.has_mean) : 0};
-  const long long nt0 = (seg0.n + kTileKeys - 1) / kTileKeys;
-  const long long n_tiles = nt0 + (seg1.n + kTileKeys - 1) / kTileKeys;
+  // tile counts fit 32 bits (at most 2^31 keys per segment, 64 per tile): the
+  // per-tile bookkeeping below stays in 32-bit scalar arithmetic
+  const int nt0 = (int)((seg0.n + kTileKeys - 1) / kTileKeys);
+  const int n_tiles = nt0 + (int)((seg1.n + kTileKeys - 1) / kTileKeys);
   // compacted rows of the own frame (masked unless token_diag), the mean rows
   // (log-count bias)
   const long long own0 = token_diag ? 0 : (long long)f * A.mk;
@@ -229,10 +231,10 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     v_off0[i] = (uint32_t)((r * seg0.vt_ld + vc * 8) * 2);
     v_off1[i] = (uint32_t)((r * seg1.vt_ld + vc * 8) * 2);
   }
-  auto issue_tile = [&](long long j, unsigned char* stage) {
+  auto issue_tile = [&](int j, unsigned char* stage) {
     const bool second = j >= nt0;
     const Segment& sg = second ? seg1 : seg0;
-    const long long u0 = (second ? j - nt0 : j) * kTileKeys;
+    const long long u0 = (long long)(second ? j - nt0 : j) * kTileKeys;
     const long long rows = min((long long)kTileKeys, sg.n - u0);
     const auto kr = buffer_rsrc(sg.k + (sg.k_row0 + u0) * rs + hoff, rows * rs * 2);
     const auto vr = buffer_rsrc(sg.vt + hoff * sg.vt_ld + sg.vt_col0 + u0,
@@ -255,35 +257,35 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
   // The order does not matter to the softmax sum.
   //   clean:  segment 0 [0, c0), segment 1 [0, a1) and [b1, m1)
   //   masked: segment 0 [c0, nt0), segment 1 [a1, min(b1, m1)) and [m1, nt1)
-  const long long nt1 = n_tiles - nt0;
-  const long long c0 = seg0.n / kTileKeys;
-  long long a1 = 0, b1 = 0, m1 = 0;
+  const int nt1 = n_tiles - nt0;
+  const int c0 = (int)(seg0.n / kTileKeys);
+  int a1 = 0, b1 = 0, m1 = 0;
   if (MODE == MODE_SUBSAMPLED) {
     const long long clean_end = A.has_mean ? min(mean0, seg1.n) : seg1.n;
-    m1 = clean_end / kTileKeys;
-    a1 = min(own0 / kTileKeys, m1);
-    b1 = (own1 + kTileKeys - 1) / kTileKeys;
+    m1 = (int)(clean_end / kTileKeys);
+    a1 = min((int)(own0 / kTileKeys), m1);
+    b1 = (int)((own1 + kTileKeys - 1) / kTileKeys);
   }
-  const long long n_clean = c0 + a1 + max(0LL, m1 - b1);
-  auto tile_of = [&](long long j) -> long long {
+  const int n_clean = c0 + a1 + max(0, m1 - b1);
+  auto tile_of = [&](int j) -> int {
     if (j < c0) return j;
     j -= c0;
     if (j < a1) return nt0 + j;
     j -= a1;
     if (j < m1 - b1) return nt0 + b1 + j;
-    j -= max(0LL, m1 - b1);
+    j -= max(0, m1 - b1);
     if (j < nt0 - c0) return c0 + j;
     j -= nt0 - c0;
-    const long long own_masked = min(b1, m1) - a1;
+    const int own_masked = min(b1, m1) - a1;
     if (j < own_masked) return nt0 + a1 + j;
     return nt0 + m1 + (j - own_masked);
   };
   // (logits in log2 units: the mean rows' bias adds as it is). Every bound is
   // taken relative to the half-tile's first key and clamped to [-1, 64], so the
   // per-score tests are 32-bit compares against wave-uniform values.
-  auto apply_mask = [&](long long j, int kb, f32x16& s) {
+  auto apply_mask = [&](int j, int kb, f32x16& s) {
     const bool second = j >= nt0;
-    const long long u0 = (second ? j - nt0 : j) * kTileKeys + kb * 32;
+    const long long u0 = (long long)(second ? j - nt0 : j) * kTileKeys + kb * 32;
     auto rel = [&](long long x) { return (int)max(-1LL, min(x - u0, 64LL)); };
     const int lim = rel(second ? seg1.n : seg0.n);
     int own_a = 64, own_b = 64, own_mean = -1, mean_a = 64;
@@ -324,8 +326,8 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
   // wait for tile j (the tiles after it in flight: min(kAhead - 1, left)), meet
   // the other waves (all done with tile j - 1's stage), refill that stage
   // (waves that issue no loads have nothing outstanding: every wait passes)
-  auto enter = [&](long long j, unsigned char* refill_stage) {
-    const long long left = n_tiles - 1 - j;
+  auto enter = [&](int j, unsigned char* refill_stage) {
+    const int left = n_tiles - 1 - j;
     if (left >= kAhead - 1) {
       wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
     } else if (kAhead > 2 && left == kAhead - 2) {
@@ -342,9 +344,9 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
   };
   // the clean tiles in whole rounds of the ring; the rest (a partial round and
   // the masked tiles) one by one with runtime stage addresses
-  const long long n_main = n_clean / kStages * kStages;
+  const int n_main = n_clean / kStages * kStages;
   auto run_rest = [&](auto&& step) {
-    for (long long j = n_main; j < n_tiles; ++j) {
+    for (int j = n_main; j < n_tiles; ++j) {
       const int cur = (int)(j % kStages);
       enter(j, smem + ((cur + kAhead) % kStages) * kStageBytes);
       step(tile_of(j), smem + cur * kStageBytes);
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     // scores already in log2 units, so c = 1
     WaveAttnState ex;
     ex.init();
-    auto step = [&](long long t, const unsigned char* stage, bool masked) {
+    auto step = [&](int t, const unsigned char* stage, bool masked) {
       f32x16 sc[2];
       ex.scores(stage, off, qB, sc);
       if (masked) {
@@ -365,14 +367,14 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
       }
       ex.consume(sc, stage, off, 1.f, false, true);
     };
-    for (long long j = 0; j < n_main; j += kStages) {
+    for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
       for (int cur = 0; cur < kStages; ++cur) {
         enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
         step(tile_of(j + cur), smem + cur * kStageBytes, false);
       }
     }
-    run_rest([&](long long t, const unsigned char* stage) { step(t, stage, true); });
+    run_rest([&](int t, const unsigned char* stage) { step(t, stage, true); });
     ex.finish(orow, lse_ptr, qvalid, 1.f);
   } else {
     // Upper bound of the query's logits (log2 units): |q'| max|k| with a margin
@@ -397,14 +399,14 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     }
     FlashWaveState st;
     st.init(bound);
-    for (long long j = 0; j < n_main; j += kStages) {
+    for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
       for (int cur = 0; cur < kStages; ++cur) {
         enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
         st.tile<false>(smem + cur * kStageBytes, off, qB, [](int, f32x16&) {});
       }
     }
-    run_rest([&](long long t, const unsigned char* stage) {
+    run_rest([&](int t, const unsigned char* stage) {
       st.tile<true>(stage, off, qB, [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
     });
     // A bound far above a row's true maximum leaves its probabilities below
