@@ -62,6 +62,10 @@ SMALL = [
     pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), 5, (4, 4), id="ragged-bf16"),
     pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), 3, (3, 2), id="ragged-f32"),
     pytest.param(Geometry(1, 1, 5, 7, 1, 64, "bf16"), 2, (2, 3), id="one-frame-bf16"),
+    # degenerate shapes: one-token frames, the most special tokens, one whole window
+    pytest.param(Geometry(5, 0, 1, 1, 1, 64, "bf16"), 3, (2, 2), id="1x1-grid-bf16"),
+    pytest.param(Geometry(2, 16, 3, 5, 2, 64, "bf16"), 2, (2, 2), id="16-specials-bf16"),
+    pytest.param(Geometry(4, 1, 4, 4, 1, 64, "f32"), 4, (4, 4), id="one-window-f32"),
 ]
 
 
