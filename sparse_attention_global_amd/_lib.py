@@ -328,7 +328,8 @@ def workspace_bytes(geom, s_h: int, s_w: int, dtype_code: int) -> int:
 
 def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
                            mean_log_count: bool = False, ws=None):
-    """AVGGT subsampled attention (mode 0) or frame attention (mode 1); see include/sga.h."""
+    """AVGGT subsampled attention (mode 0), frame attention (mode 1) or the
+    token-level diagonal (mode 2); see include/sga.h."""
     T, H, d = tokens(geom), geom.n_heads, 64
     _need(q, "q", T, H, d)
     _need(k, "k", T, H, d, q.dtype)

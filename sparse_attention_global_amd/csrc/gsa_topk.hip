@@ -15,13 +15,17 @@
 // whose dropped term and residuals are ~2^-16 relative -- far inside the 1e-3
 // score gap the selection is checked at. The 1/sqrt(64) scale is exact.
 //
-// Work split: a workgroup of W waves owns 32*W query blocks of one head; every
-// wave owns 32 of them and streams all pooled keys in tiles of 64 through LDS
-// (double buffered). Each lane keeps, for its query block, a threshold (the
-// current K-th best); a tile whose lane-wise maximum stays below it costs one
-// max tree and one compare. Candidates that beat it are inserted into a sorted
-// per-block list in LDS, one half-wave at a time so the two lanes sharing a
-// block never race.
+// Work split, common to the kernels below: a workgroup owns 32 query blocks
+// of one head per wave and streams the competing pooled keys in tiles of 64
+// through LDS (double buffered); in the MFMA layout the lanes l and l + 32
+// hold the same query block's scores for different keys. Three selections:
+//   top_k <= 16:     per-lane sorted register lists, merged at the end
+//                    (gsa_topk_reg_kernel);
+//   16 < top_k:      a score bound, then a filter and a wave-wide sort
+//                    (gsa_topk_bound_kernel, gsa_topk_wide_kernel);
+//   its fallback:    sorted per-block lists in LDS, inserted one half-wave at
+//                    a time (gsa_topk_kernel), for the blocks the filter
+//                    could not hold.
 #include "common.hpp"
 #include "kernels.hpp"
 
