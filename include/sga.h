@@ -136,9 +136,10 @@ enum { SGA_KEEP_SPECIAL = 1, SGA_KEEP_REF_FRAME = 2 };
  * score (nullable): [H, N*nqb, top_k] fp32, the score of each idx entry.
  * 1 <= top_k <= min(competing keys, 128); competing keys = N*nb, or (N-1)*nb
  * with SGA_KEEP_REF_FRAME.
- * ws: sga_workspace_size(geom, SGA_OP_TOPK, top_k, keep, &bytes) bytes: none
- *   for top_k <= 16; above, the candidate buffers of the threshold-and-sort
- *   selection (at most 1 GiB) and one flag byte per (head, query block).
+ * ws: sga_workspace_size(geom, SGA_OP_TOPK, top_k, keep, &bytes) bytes: the
+ *   pooled keys split into bf16 hi/lo planes (N*nb*H*256 bytes); for
+ *   top_k > 16 then the candidate buffers of the threshold-and-sort selection
+ *   (at most 1 GiB), a score bound and a flag byte per (head, query block).
  */
 sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_blk_f32,
                            const float* k_cmp_f32, int32_t top_k, int32_t keep,

@@ -486,6 +486,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 50000; }
+int32_t sga_version(void) { return 60000; }
 
 }  // extern "C"

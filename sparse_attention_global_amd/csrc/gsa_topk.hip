@@ -54,6 +54,77 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
 
 // only (nullable): per (head, query block) flags; a workgroup none of whose
 // blocks is flagged returns at once (the wide kernel's overflow fallback).
+// ---------------------------------------------------------------------------
+// Key planes: the competing pooled keys split once into bf16 hi and lo parts,
+// per head and key 64 hi values then 64 lo values (256 bytes), so that a
+// 64-key tile is one contiguous 16 KiB run of a head that loads straight into
+// LDS (16-byte buffer loads into LDS: no VGPR staging, no conversion in the
+// selection loops).
+// ---------------------------------------------------------------------------
+constexpr int kPlaneRowBytes = 256;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
+}
+// Lane l's 16 bytes at rsrc + voff land at lds_dst + 16 l (lds_dst wave-uniform);
+// a lane reading past the extent gets zeros.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, unsigned char* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
+// planes[h][key] = (hi[64], lo[64]) of k_cmp[key, h, :]: a thread per 8 values.
+__global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict__ k_cmp, long long n_keys,
+                                                        int n_heads, u32x4* __restrict__ planes) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_keys * n_heads * 8) return;
+  const int chunk = (int)(i & 7);
+  const long long kh = i >> 3;
+  const long long key = kh / n_heads;
+  const int h = (int)(kh % n_heads);
+  const float* src = k_cmp + kh * kHeadDim + chunk * 8;
+  float x[8];
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  u32x4 hi, lo;
+  split8(x, hi, lo);
+  u32x4* dst = planes + ((long long)h * n_keys + key) * (kPlaneRowBytes / 16);
+  dst[chunk] = hi;
+  dst[8 + chunk] = lo;
+}
+
+// Loads 64-key tiles of one head's planes into an LDS stage laid out as the
+// MFMA reads want it: the hi plane (8 KiB) then the lo plane, key row r at
+// r * 128 bytes, logical 16-byte chunk c at physical chunk c ^ (r & 7). Each
+// of the 256 threads issues 4 loads per tile; its source chunks are fixed.
+struct PlaneTiles {
+  const unsigned char* head;  // this head's planes at the first competing key
+  long long n_keys;           // competing keys
+  uint32_t voff[4];
+
+  __device__ __forceinline__ void init(const void* planes, long long n_total, int h, long long first,
+                                       long long n_cand, int tid) {
+    head = static_cast<const unsigned char*>(planes) + ((long long)h * n_total + first) * kPlaneRowBytes;
+    n_keys = n_cand;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int o = q * 4096 + tid * 16;      // LDS byte offset this thread fills
+      const int plane = o >> 13, r = (o & 8191) >> 7, pc = (o >> 4) & 7;
+      voff[q] = (uint32_t)(r * kPlaneRowBytes + plane * 128 + ((pc ^ (r & 7)) << 4));
+    }
+  }
+  // keys u0 .. u0 + 63 into `stage` (rows past the end load as zeros)
+  __device__ __forceinline__ void issue(long long u0, unsigned char* stage, int wave) const {
+    const long long rows = min((long long)kTileN, n_keys - u0);
+    const auto rsrc = buffer_rsrc(head + u0 * kPlaneRowBytes, rows * kPlaneRowBytes);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_dma16(rsrc, voff[q], stage + q * 4096 + wave * 1024);
+  }
+};
+
 __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __restrict__ q_blk,
                                                        const float* __restrict__ k_cmp,
                                                        long long n_cand, int j0,
@@ -261,8 +332,8 @@ __device__ __forceinline__ bool better(float s, int j, float ts, int tj) {
 // 2.46 ms against 2.76 ms at 3 waves per SIMD and 3.40 ms at 2.
 template <bool FULL>  // FULL: top_k == kRegK, the threshold is the list's last slot
 __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const float* __restrict__ q_blk,
-                                                           const float* __restrict__ k_cmp,
-                                                           long long n_cand, int j0,
+                                                           const void* __restrict__ planes,
+                                                           long long n_total, long long n_cand, int j0,
                                                            int top_k, int n_rowtiles,
                                                            int32_t* __restrict__ idx,
                                                            float* __restrict__ score) {
@@ -297,39 +368,8 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
     }
   }
 
-  // loader: thread -> (key tid>>2 of the tile, d range 16*(tid&3) .. +16)
-  f32x4 kreg[4];
-  auto load_tile = [&](long long u0) {
-    const long long u = u0 + (tid >> 2);
-    const int quarter = tid & 3;
-    if (u < n_cand) {
-      const float* kp = k_cmp + u * rs + hoff + quarter * 16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kreg[e] = *reinterpret_cast<const f32x4*>(kp + 4 * e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kreg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  auto store_tile = [&](int stage) {
-    unsigned char* hi_p = smem + stage * kStageBytes;
-    unsigned char* lo_p = hi_p + kTileBytes;
-    const int key = tid >> 2, quarter = tid & 3;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = kreg[2 * half][e];
-        x[4 + e] = kreg[2 * half + 1][e];
-      }
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      const int chunk = 2 * quarter + half;
-      st16(hi_p + t_off(key, chunk), hi);
-      st16(lo_p + t_off(key, chunk), lo);
-    }
-  };
+  PlaneTiles tiles;
+  tiles.init(planes, n_total, h, j0, n_cand, tid);
 
   float lv[kRegK];
   int lj[kRegK];
@@ -339,15 +379,16 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   const int kth = top_k - 1;
 
   const long long n_tiles = (n_cand + kTileN - 1) / kTileN;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  tiles.issue(0, smem, wave);
 
   for (long long it = 0; it < n_tiles; ++it) {
     const int stage = (int)(it & 1);
     const long long u0 = it * kTileN;
     const bool more = it + 1 < n_tiles;
-    if (more) load_tile(u0 + kTileN);
+    // tile it has landed in every wave's loads, and every wave is done with
+    // the other stage (the barrier's fence waits for this wave's loads)
+    __syncthreads();
+    if (more) tiles.issue(u0 + kTileN, smem + (stage ^ 1) * kStageBytes, wave);
     const unsigned char* hi_p = smem + stage * kStageBytes;
     const unsigned char* lo_p = hi_p + kTileBytes;
 
@@ -417,8 +458,6 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
           }
         }
     }
-    if (more) store_tile(stage ^ 1);
-    __syncthreads();
   }
 
   // ---- merge the block's two lists (lanes l and l + 32) ------------------------
@@ -508,11 +547,10 @@ constexpr long long kWideSlotKeys = (long long)kWideRows * 2 * kWideCap;
 // past the end scored -inf).
 struct ScoreStream {
   unsigned char* smem;
-  const float* k_cmp;
+  PlaneTiles tiles;
   long long n_cand, rs, hoff;
-  int tid, li, hh;
+  int tid, wave, li, hh;
   u32x4 qh[4], ql[4];
-  f32x4 kreg[4];
 
   __device__ __forceinline__ void load_q(const float* q_blk, long long row, bool rvalid) {
     // scaled by 1/sqrt(64) = 1/8 (exact), hi and lo planes
@@ -530,49 +568,20 @@ struct ScoreStream {
       split8(x, qh[ks], ql[ks]);
     }
   }
-  __device__ __forceinline__ void load_tile(long long u0) {
-    const long long u = u0 + (tid >> 2);
-    const int quarter = tid & 3;
-    if (u < n_cand) {
-      const float* kp = k_cmp + u * rs + hoff + quarter * 16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kreg[e] = *reinterpret_cast<const f32x4*>(kp + 4 * e);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kreg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  __device__ __forceinline__ void store_tile(int stage) {
-    unsigned char* hi_p = smem + stage * kStageBytes;
-    unsigned char* lo_p = hi_p + kTileBytes;
-    const int key = tid >> 2, quarter = tid & 3;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = kreg[2 * half][e];
-        x[4 + e] = kreg[2 * half + 1][e];
-      }
-      u32x4 hi, lo;
-      split8(x, hi, lo);
-      const int chunk = 2 * quarter + half;
-      st16(hi_p + t_off(key, chunk), hi);
-      st16(lo_p + t_off(key, chunk), lo);
-    }
-  }
   // tiles it = 0, stride, 2*stride, ... of the key range
   template <class Visit>
   __device__ __forceinline__ void run(int stride, Visit&& visit) {
     const long long n_ktiles = (n_cand + kTileN - 1) / kTileN;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    __syncthreads();  // every wave is done with the stages of a previous stream
+    tiles.issue(0, smem, wave);
     int stage = 0;
     for (long long it = 0; it < n_ktiles; it += stride) {
       const long long u0 = it * kTileN;
       const bool more = it + stride < n_ktiles;
-      if (more) load_tile(u0 + (long long)stride * kTileN);
+      // tile it has landed (the barrier's fence waits for this wave's loads)
+      // and every wave is done with the other stage
+      __syncthreads();
+      if (more) tiles.issue(u0 + (long long)stride * kTileN, smem + (stage ^ 1) * kStageBytes, wave);
       const unsigned char* hi_p = smem + stage * kStageBytes;
       const unsigned char* lo_p = hi_p + kTileBytes;
       f32x16 s[2];
@@ -601,8 +610,6 @@ struct ScoreStream {
           }
       }
       visit(s, u0);
-      if (more) store_tile(stage ^ 1);
-      __syncthreads();
       stage ^= 1;
     }
   }
@@ -610,7 +617,8 @@ struct ScoreStream {
 
 template <int DEPTH>
 __global__ __launch_bounds__(256, 2) void gsa_topk_bound_kernel(Geom g, const float* __restrict__ q_blk,
-                                                               const float* __restrict__ k_cmp,
+                                                               const void* __restrict__ planes,
+                                                               long long n_total, long long first,
                                                                long long n_cand, int top_k,
                                                                int n_rowtiles,
                                                                float* __restrict__ bound) {
@@ -627,11 +635,12 @@ __global__ __launch_bounds__(256, 2) void gsa_topk_bound_kernel(Geom g, const fl
 
   ScoreStream st;
   st.smem = smem;
-  st.k_cmp = k_cmp;
+  st.tiles.init(planes, n_total, h, first, n_cand, tid);
   st.n_cand = n_cand;
   st.rs = (long long)g.n_heads * kHeadDim;
   st.hoff = (long long)h * kHeadDim;
   st.tid = tid;
+  st.wave = wave;
   st.li = li;
   st.hh = hh;
   st.load_q(q_blk, row, rvalid);
@@ -761,7 +770,8 @@ __device__ __forceinline__ void select_block(const uint64_t* __restrict__ rb, in
 }
 
 __global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const float* __restrict__ q_blk,
-                                                              const float* __restrict__ k_cmp,
+                                                              const void* __restrict__ planes,
+                                                              long long n_total,
                                                               long long n_cand, int j0, int top_k,
                                                               int n_rowtiles, long long n_tiles,
                                                               const float* __restrict__ bound,
@@ -781,10 +791,10 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const flo
 
   ScoreStream st;
   st.smem = smem;
-  st.k_cmp = k_cmp;
   st.n_cand = n_cand;
   st.rs = (long long)g.n_heads * kHeadDim;
   st.tid = tid;
+  st.wave = wave;
   st.li = li;
   st.hh = hh;
 
@@ -794,6 +804,7 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const flo
     const long long row = row0 + wave * 32 + li;
     const bool rvalid = row < n_rows;
     st.hoff = (long long)h * kHeadDim;
+    st.tiles.init(planes, n_total, h, j0, n_cand, tid);
     st.load_q(q_blk, row, rvalid);
     const float tau = rvalid ? bound[(long long)h * n_rows + row] : INFINITY;
 
@@ -865,12 +876,18 @@ int resident_workgroups(const void* kernel, int threads, size_t lds) {
 
 static size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Workspace: the key planes (every pooled key, N*nb*H*256 bytes); for wide
+// selection then the per-workgroup key buffers, the bounds and the flags.
+static size_t planes_bytes(const Geom& g) {
+  return round_up256((size_t)g.n_frames * g.nb * g.n_heads * kPlaneRowBytes);
+}
+
 size_t gsa_topk_workspace(const Geom& g, int top_k) {
-  if (top_k <= kRegK) return 0;
+  if (top_k <= kRegK) return planes_bytes(g);
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const long long tiles = (n_rows + kWideRows - 1) / kWideRows * g.n_heads;
   const long long slots = tiles < kWideMaxSlots ? tiles : kWideMaxSlots;
-  return round_up256((size_t)slots * kWideSlotKeys * sizeof(uint64_t)) +
+  return planes_bytes(g) + round_up256((size_t)slots * kWideSlotKeys * sizeof(uint64_t)) +
          round_up256((size_t)(n_rows * g.n_heads) * sizeof(float)) +
          round_up256((size_t)(n_rows * g.n_heads));
 }
@@ -878,20 +895,31 @@ size_t gsa_topk_workspace(const Geom& g, int top_k) {
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
                            int first, int32_t* idx, float* score, void* ws, hipStream_t stream) {
   const long long n_rows = (long long)g.n_frames * g.nqb;
+  const long long n_total = (long long)g.n_frames * g.nb;
   // the kernels see the competing keys only, indexed from 0, and add `first`
   // to the indices they write
-  const long long n_cand = (long long)g.n_frames * g.nb - first;
-  const float* kc = k_cmp + (long long)first * g.n_heads * kHeadDim;
+  const long long n_cand = n_total - first;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  void* planes = w;
+  w += planes_bytes(g);
+  {
+    const long long n = n_total * g.n_heads * 8;
+    const long long blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cmp, n_total,
+                       g.n_heads, static_cast<u32x4*>(planes));
+    if (hipError_t e = hipGetLastError()) return e;
+  }
   if (top_k <= kRegK) {
     const int n_rowtiles = (int)((n_rows + 127) / 128);
     const long long grid = (long long)n_rowtiles * g.n_heads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (top_k == kRegK) {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<true>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score);
     } else {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<false>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, kc, n_cand, first, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score);
     }
     return hipGetLastError();
   }
@@ -901,7 +929,6 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
   const long long tiles = (long long)n_rowtiles * g.n_heads;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
   const long long slots = tiles < kWideMaxSlots ? tiles : kWideMaxSlots;
-  unsigned char* w = static_cast<unsigned char*>(ws);
   uint64_t* buf = reinterpret_cast<uint64_t*>(w);
   w += round_up256((size_t)slots * kWideSlotKeys * sizeof(uint64_t));
   float* bound = reinterpret_cast<float*>(w);
@@ -909,18 +936,19 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
   uint8_t* flags = reinterpret_cast<uint8_t*>(w);
   if (top_k <= 64) {
     hipLaunchKernelGGL(gsa_topk_bound_kernel<2>, dim3((unsigned)tiles), dim3(256), 2 * kStageBytes, stream,
-                       g, q_blk, kc, n_cand, top_k, n_rowtiles, bound);
+                       g, q_blk, planes, n_total, (long long)first, n_cand, top_k, n_rowtiles, bound);
   } else {
     hipLaunchKernelGGL(gsa_topk_bound_kernel<4>, dim3((unsigned)tiles), dim3(256), 2 * kStageBytes, stream,
-                       g, q_blk, kc, n_cand, top_k, n_rowtiles, bound);
+                       g, q_blk, planes, n_total, (long long)first, n_cand, top_k, n_rowtiles, bound);
   }
   if (hipError_t e = hipGetLastError()) return e;
   const size_t lds_wide = 2 * kStageBytes + 4 * 128 * sizeof(uint64_t);
   long long grid = resident_workgroups(reinterpret_cast<const void*>(gsa_topk_wide_kernel), 256, lds_wide);
   if (grid > slots) grid = slots;
-  hipLaunchKernelGGL(gsa_topk_wide_kernel, dim3((unsigned)grid), dim3(256), lds_wide, stream, g, q_blk, kc,
-                     n_cand, first, top_k, n_rowtiles, tiles, bound, buf, flags, idx, score);
+  hipLaunchKernelGGL(gsa_topk_wide_kernel, dim3((unsigned)grid), dim3(256), lds_wide, stream, g, q_blk, planes,
+                     n_total, n_cand, first, top_k, n_rowtiles, tiles, bound, buf, flags, idx, score);
   if (hipError_t e = hipGetLastError()) return e;
+  const float* kc = k_cmp + (long long)first * g.n_heads * kHeadDim;
   int waves = 4;
   auto lds_for = [&](int w) { return (size_t)2 * kStageBytes + (size_t)w * 32 * (top_k + 1) * 8; };
   if (lds_for(waves) > 160 * 1024) waves = 2;

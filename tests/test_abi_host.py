@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 50000
+    assert library().sga_version() == 60000
 
 
 def geom(**kw):
@@ -198,17 +198,19 @@ def test_fine_workspace():
 def test_topk_workspace():
     g = geom(n_frames=256)
     n_rows = 256 * 101
-    # top_k <= 16: the register kernel needs nothing
-    assert _ws(g, 4, 16, 0) == (OK, 0)
-    # wider: one 1 MiB key buffer per persistent workgroup (128 blocks x 2 lanes
-    # x 512 keys x 8 bytes), at most 1024 of them, then a score bound (fp32)
-    # and a flag byte per (head, query block)
+    # every width: the pooled keys split into bf16 hi/lo planes (256 bytes per
+    # key and head)
+    planes = r256(256 * 100 * 16 * 256)
+    assert _ws(g, 4, 16, 0) == (OK, planes)
+    # wider: then one 1 MiB key buffer per persistent workgroup (128 blocks x 2
+    # lanes x 512 keys x 8 bytes), at most 1024 of them, then a score bound
+    # (fp32) and a flag byte per (head, query block)
     tiles = -(-n_rows // 128) * 16
-    assert _ws(g, 4, 17, 0) == (OK, min(tiles, 1024) * (1 << 20) + r256(n_rows * 16 * 4)
+    assert _ws(g, 4, 17, 0) == (OK, planes + min(tiles, 1024) * (1 << 20) + r256(n_rows * 16 * 4)
                                 + r256(n_rows * 16))
     small = geom(n_frames=3, n_heads=2)
-    assert _ws(small, 4, 20, 0) == (OK, 3 * 2 * (1 << 20) + r256(3 * 101 * 2 * 4)
-                                    + r256(3 * 101 * 2))  # 3 row tiles x 2 heads
+    assert _ws(small, 4, 20, 0) == (OK, r256(3 * 100 * 2 * 256) + 3 * 2 * (1 << 20)
+                                    + r256(3 * 101 * 2 * 4) + r256(3 * 101 * 2))  # 3 row tiles x 2 heads
     assert _ws(g, 4, 129, 0)[0] == INVALID
     assert _ws(geom(n_frames=1), 4, 20, 2)[0] == INVALID
     # a missing workspace is reported before anything is launched
