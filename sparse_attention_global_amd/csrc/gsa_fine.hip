@@ -98,41 +98,57 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
   // ---- each wave's selected windows, private LDS stage -----------------------
   unsigned char* my_stage = smem + wave * kTileStageBytes;
   const int n_t2 = (A.top_k + 3) / 4;
-  for (int sd = 0; sd < 2; ++sd) {
+  // tiles it = sd * n_t2 + t: block b_wave + sd, windows 4t .. 4t + 3; the
+  // next tile's keys and values are loaded into registers while this one runs
+  u32x4 kreg[4][2], vreg[4][2];
+  bool have[4][2];
+  auto gather = [&](int it) {
+    const int sd = it / n_t2, t = it % n_t2;
     const long long b = b_wave + sd;
     const bool bvalid = b < n_qb;
     const int32_t* sel = A.idx + ((long long)h * n_qb + (bvalid ? b : 0)) * A.top_k;
-    for (int t = 0; t < n_t2; ++t) {
-      // lane -> key pair 2 ((lane >> 3) + 8 part), chunk lane & 7; key u = 16 * window + slot
 #pragma unroll
-      for (int part = 0; part < 4; ++part) {
-        const int u = 2 * ((lane >> 3) + 8 * part);
-        u32x4 kreg[2], vreg[2];
-        long long rows[2];
+    for (int part = 0; part < 4; ++part) {
+      const int u = 2 * ((lane >> 3) + 8 * part);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int wi = 4 * t + ((u + i) >> 4);
-          long long row = -1;
-          if (bvalid && wi < A.top_k) row = window_slot_row(g, A.w_lo, sel[wi], (u + i) & 15);
-          rows[i] = row;
-          if (row >= 0) {
-            kreg[i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
-            vreg[i] = ld16(A.v + row * rs + hoff + (lane & 7) * 8);
-          } else {
-            kreg[i] = u32x4{0, 0, 0, 0};
-            vreg[i] = u32x4{0, 0, 0, 0};
-          }
-        }
-        tile_store_kv_pair(my_stage, u, lane & 7, kreg[0], kreg[1], vreg[0], vreg[1]);
-        if ((lane & 7) == 0) {
-          tile_bias(my_stage)[u] = rows[0] >= 0 ? 0.f : -INFINITY;
-          tile_bias(my_stage)[u + 1] = rows[1] >= 0 ? 0.f : -INFINITY;
+      for (int i = 0; i < 2; ++i) {
+        const int wi = 4 * t + ((u + i) >> 4);
+        long long row = -1;
+        if (bvalid && wi < A.top_k) row = window_slot_row(g, A.w_lo, sel[wi], (u + i) & 15);
+        have[part][i] = row >= 0;
+        if (row >= 0) {
+          kreg[part][i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
+          vreg[part][i] = ld16(A.v + row * rs + hoff + (lane & 7) * 8);
+        } else {
+          kreg[part][i] = u32x4{0, 0, 0, 0};
+          vreg[part][i] = u32x4{0, 0, 0, 0};
         }
       }
-      __syncthreads();
-      st.step(my_stage, off, qB, c, true, side == sd && bvalid);
-      __syncthreads();
     }
+  };
+  const int n_it = 2 * n_t2;
+  gather(0);
+  for (int it = 0; it < n_it; ++it) {
+    const int sd = it / n_t2;
+    const bool bvalid = b_wave + sd < n_qb;
+#pragma unroll
+    for (int part = 0; part < 4; ++part) {
+      const int u = 2 * ((lane >> 3) + 8 * part);
+      tile_store_kv_pair(my_stage, u, lane & 7, kreg[part][0], kreg[part][1], vreg[part][0], vreg[part][1]);
+      if ((lane & 7) == 0) {
+        tile_bias(my_stage)[u] = have[part][0] ? 0.f : -INFINITY;
+        tile_bias(my_stage)[u + 1] = have[part][1] ? 0.f : -INFINITY;
+      }
+    }
+    if (it + 1 < n_it) gather(it + 1);
+    // the stage is this wave's own: a wave-level wait and barrier suffice
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    st.step(my_stage, off, qB, c, true, side == sd && bvalid);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   st.finish(A.o + (qvalid ? qrow : 0) * rs + hoff,
