@@ -509,6 +509,20 @@ def test_deterministic():
         assert torch.equal(a[key], c[key]), key
     assert torch.equal(d1, d2)
     assert torch.equal(s1, s2)
+    # the variants: bit-identical repeats too (the wide selection's persistent
+    # workgroups and per-lane buffers involve no atomics or races)
+    for kw in (dict(top_k=128), dict(top_k=16, keep_ref=True), dict(top_k=16, pooled_q=True),
+               dict(top_k=16, include_pad=True)):
+        top_k = kw.pop("top_k")
+        e = sga.gsa_layer(q, k, v, w, b, geom, top_k, keep_intermediates=True, **kw)
+        f = sga.gsa_layer(q, k, v, w, b, geom, top_k, keep_intermediates=True, **kw)
+        _sync()
+        for key in e:
+            assert torch.equal(e[key], f[key]), (kw, key)
+    t1 = sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=2)
+    t2 = sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=2)
+    _sync()
+    assert torch.equal(t1, t2)
 
 
 # ---------------------------------------------------------------------------
