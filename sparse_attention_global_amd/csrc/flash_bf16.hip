@@ -135,14 +135,17 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
       rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16, (int)voff, 0, 0, 0);
 }
 
-// Wait until at most N direct loads of this lane are in flight, then meet the
-// other waves: every wave's loads of the tile about to be read have landed and
-// every wave is done reading the stage about to be refilled.
+// Wait until at most N direct loads of this lane are in flight and its LDS
+// reads have returned, then meet the other waves: every wave's loads of the
+// tile about to be read have landed and every wave is done reading the stage
+// about to be refilled. (The compiler may leave a tile's last LDS reads in
+// flight across the barrier, their MFMAs after it; lgkmcnt(0) keeps the refill
+// of that stage behind them.)
 template <int N>
 __device__ __forceinline__ void wait_and_meet() {
   static_assert(N >= 0 && N < 64, "vmcnt field");
-  // vmcnt <= N (bits 3:0 and 15:14); lgkmcnt, expcnt unconstrained
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  // vmcnt <= N (bits 3:0 and 15:14), lgkmcnt = 0 (bits 11:8), expcnt unconstrained
+  __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -231,14 +234,29 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     v_off0[i] = (uint32_t)((r * seg0.vt_ld + vc * 8) * 2);
     v_off1[i] = (uint32_t)((r * seg1.vt_ld + vc * 8) * 2);
   }
+  // Per segment, fixed for the kernel: the byte address of this head's first K
+  // row and first V^T column, the V^T extent and the key count. A tile then
+  // costs one 32x32-bit product and a few adds on the scalar unit; the key and
+  // byte counts fit 31 bits (checked at launch).
+  const int row_bytes = (int)(rs * 2);
+  const char* const kb0 = reinterpret_cast<const char*>(seg0.k + seg0.k_row0 * rs + hoff);
+  const char* const vb0 = reinterpret_cast<const char*>(seg0.vt + hoff * seg0.vt_ld + seg0.vt_col0);
+  const int vbytes0 = (int)(kHeadDim * seg0.vt_ld * 2), n0 = (int)seg0.n;
+  const char* kb1 = kb0;
+  const char* vb1 = vb0;
+  int vbytes1 = vbytes0, n1 = n0;
+  if (MODE == MODE_SUBSAMPLED) {
+    kb1 = reinterpret_cast<const char*>(seg1.k + seg1.k_row0 * rs + hoff);
+    vb1 = reinterpret_cast<const char*>(seg1.vt + hoff * seg1.vt_ld + seg1.vt_col0);
+    vbytes1 = (int)(kHeadDim * seg1.vt_ld * 2);
+    n1 = (int)seg1.n;
+  }
   auto issue_tile = [&](int j, unsigned char* stage) {
-    const bool second = j >= nt0;
-    const Segment& sg = second ? seg1 : seg0;
-    const long long u0 = (long long)(second ? j - nt0 : j) * kTileKeys;
-    const long long rows = min((long long)kTileKeys, sg.n - u0);
-    const auto kr = buffer_rsrc(sg.k + (sg.k_row0 + u0) * rs + hoff, rows * rs * 2);
-    const auto vr = buffer_rsrc(sg.vt + hoff * sg.vt_ld + sg.vt_col0 + u0,
-                                kHeadDim * sg.vt_ld * 2);
+    const bool second = MODE == MODE_SUBSAMPLED && j >= nt0;
+    const int u0 = (second ? j - nt0 : j) * kTileKeys;
+    const int rows = min(kTileKeys, (second ? n1 : n0) - u0);
+    const auto kr = buffer_rsrc((second ? kb1 : kb0) + (long long)u0 * row_bytes, rows * row_bytes);
+    const auto vr = buffer_rsrc((second ? vb1 : vb0) + 2LL * u0, second ? vbytes1 : vbytes0);
     unsigned char* kdst = stage + wave_u * kRowsPerWave * 128;
     unsigned char* vdst = kdst + kTileKBytes;
     if (C::dma_waves < C::waves && wave_u >= C::dma_waves) return;
@@ -251,34 +269,52 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
 
   // ---- tile order: every clean tile first, the masked ones after -------------
   // Tile t (t < nt0: segment 0, else segment 1 tile t - nt0) needs a logit mask
-  // or bias when it holds a segment's end, the query frame's own compacted rows
-  // or mean rows. Those few tiles run after the clean ones, in a loop of their
-  // own, so that the masking code never occupies registers of the main loop.
-  // The order does not matter to the softmax sum.
-  //   clean:  segment 0 [0, c0), segment 1 [0, a1) and [b1, m1)
-  //   masked: segment 0 [c0, nt0), segment 1 [a1, min(b1, m1)) and [m1, nt1)
+  // or bias when it holds a segment's end, the query frame's own compacted rows,
+  // the own frame's mean row, or mean rows that carry the log-count bias. Those
+  // few tiles run after the clean ones, in a loop of their own, so that the
+  // masking code never occupies registers of the main loop. The order does not
+  // matter to the softmax sum. Unbiased mean rows are ordinary keys, so only the
+  // tile tm holding the own frame's mean row leaves the clean range (when it
+  // lies in [b1, m1); elsewhere it is masked already).
+  //   clean:  segment 0 [0, c0), segment 1 [0, a1) and [b1, m1) without tm
+  //   masked: segment 0 [c0, nt0), segment 1 [a1, min(b1, m1)), tm, [m1, nt1)
   const int nt1 = n_tiles - nt0;
   const int c0 = (int)(seg0.n / kTileKeys);
-  int a1 = 0, b1 = 0, m1 = 0;
+  int a1 = 0, b1 = 0, m1 = 0, tm = 0x7fffffff;
   if (MODE == MODE_SUBSAMPLED) {
-    const long long clean_end = A.has_mean ? min(mean0, seg1.n) : seg1.n;
+    const bool mean_biased = A.has_mean && A.mean_bias2 != 0.f;
+    const long long clean_end = mean_biased ? min(mean0, seg1.n) : seg1.n;
     m1 = (int)(clean_end / kTileKeys);
     a1 = min((int)(own0 / kTileKeys), m1);
     b1 = (int)((own1 + kTileKeys - 1) / kTileKeys);
+    if (A.has_mean && !mean_biased && !token_diag) {
+      const int t = (int)((mean0 + f) / kTileKeys);
+      if (t >= b1 && t < m1) tm = t;
+    }
   }
-  const int n_clean = c0 + a1 + max(0, m1 - b1);
+  const int ex = tm != 0x7fffffff ? 1 : 0;
+  const int n_r2 = max(0, m1 - b1) - ex;
+  const int n_clean = c0 + a1 + n_r2;
   auto tile_of = [&](int j) -> int {
     if (j < c0) return j;
     j -= c0;
     if (j < a1) return nt0 + j;
     j -= a1;
-    if (j < m1 - b1) return nt0 + b1 + j;
-    j -= max(0, m1 - b1);
+    if (j < n_r2) {
+      const int t = b1 + j;
+      return nt0 + t + (t >= tm ? 1 : 0);
+    }
+    j -= n_r2;
     if (j < nt0 - c0) return c0 + j;
     j -= nt0 - c0;
     const int own_masked = min(b1, m1) - a1;
     if (j < own_masked) return nt0 + a1 + j;
-    return nt0 + m1 + (j - own_masked);
+    j -= own_masked;
+    if (ex) {
+      if (j == 0) return nt0 + tm;
+      --j;
+    }
+    return nt0 + m1 + j;
   };
   // (logits in log2 units: the mean rows' bias adds as it is). Every bound is
   // taken relative to the half-tile's first key and clamped to [-1, 64], so the
@@ -342,9 +378,23 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     }
     if (j + kAhead < n_tiles) issue_tile(tile_of(j + kAhead), refill_stage);
   };
-  // the clean tiles in whole rounds of the ring; the rest (a partial round and
-  // the masked tiles) one by one with runtime stage addresses
-  const int n_main = n_clean / kStages * kStages;
+  // The clean tiles in whole rounds of the ring while the tile issued ahead is
+  // clean as well: its index then comes from the three clean ranges alone and
+  // every wait keeps kAhead - 1 tiles in flight. The rest (a partial round, the
+  // last kAhead clean tiles and the masked ones) run one by one with runtime
+  // stage addresses.
+  auto clean_tile = [&](int j) -> int {
+    if (j < c0) return j;
+    j -= c0;
+    if (j < a1) return nt0 + j;
+    const int t = b1 + (j - a1);
+    return nt0 + t + (t >= tm ? 1 : 0);
+  };
+  auto enter_clean = [&](int j, unsigned char* refill_stage) {
+    wait_and_meet<(kAhead - 1) * kLoadsPerTile>();
+    issue_tile(clean_tile(j + kAhead), refill_stage);
+  };
+  const int n_main = max(0, n_clean - kAhead) / kStages * kStages;
   auto run_rest = [&](auto&& step) {
     for (int j = n_main; j < n_tiles; ++j) {
       const int cur = (int)(j % kStages);
@@ -370,8 +420,8 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
       for (int cur = 0; cur < kStages; ++cur) {
-        enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
-        step(tile_of(j + cur), smem + cur * kStageBytes, false);
+        enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+        step(clean_tile(j + cur), smem + cur * kStageBytes, false);
       }
     }
     run_rest([&](int t, const unsigned char* stage) { step(t, stage, true); });
@@ -402,7 +452,7 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
       for (int cur = 0; cur < kStages; ++cur) {
-        enter(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+        enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
         st.tile<false>(smem + cur * kStageBytes, off, qB, [](int, f32x16&) {});
       }
     }

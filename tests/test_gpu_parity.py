@@ -521,8 +521,12 @@ def test_deterministic():
             assert torch.equal(e[key], f[key]), (kw, key)
     t1 = sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=2)
     t2 = sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=2)
+    f1 = sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=1)
+    f2 = sga.dense_global_attn(q, k, v, geom, frame_local=True)
+    f3 = sga.dense_global_attn(q, k, v, geom, frame_local=True)
     _sync()
     assert torch.equal(t1, t2)
+    assert torch.equal(f1, f2) and torch.equal(f2, f3)
 
 
 # ---------------------------------------------------------------------------
@@ -643,7 +647,14 @@ def _sga_check(name, rows_cap=None):
     o = sga.subsampled_global_attn(q, k, v, geom, sh, sw)
     of = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=1)
     od = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=2)
+    # repeats are bit-identical: a stage refilled while another wave still
+    # reads it would show here first (hundreds of workgroups per CU in turn)
+    o2 = sga.subsampled_global_attn(q, k, v, geom, sh, sw)
+    of2 = sga.subsampled_global_attn(q, k, v, geom, sh, sw, mode=1)
     _sync()
+    assert torch.equal(o, o2), f"{name} subsampled repeat differs"
+    assert torch.equal(of, of2), f"{name} frame repeat differs"
+    del o2, of2
     qh, kh, vh = host(q), host(k), host(v)
     W = oracle_workers()
     assert_close(host(o)[rows], oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, rows=rows,
