@@ -17,9 +17,10 @@
 // head; each wave owns two of them as the 32 MFMA columns (block b0 in columns
 // 0..15, block b0 + 1 in columns 16..31, member m of a 4x4 window at grid
 // offset (m / 4, m % 4); a specials block holds its S tokens). Each wave
-// gathers its own blocks' selected tokens (top_k windows x 16 slots, 64 keys =
-// 4 windows per tile) into a private LDS stage; while one block's keys are
-// processed the other block's 16 columns sit out.
+// gathers its own blocks' selected tokens into a private LDS stage, packed
+// without gaps: a tile takes the next selected windows whose in-grid tokens
+// fit 64 keys (4 whole windows, up to 64 one-token corner windows). While one
+// block's keys are processed the other block's 16 columns sit out.
 #include "attn_tile.hpp"
 #include "kernels.hpp"
 
@@ -29,6 +30,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 256;
 constexpr int kBlocksPerWG = 2 * kWaves;
+// per wave: its LDS stage plus the token rows of the tile being gathered
+constexpr int kWaveLdsBytes = kTileStageBytes + kTileKeys * 4;
 
 struct FineArgs {
   const bf16* q;
@@ -57,14 +60,21 @@ __device__ __forceinline__ long long block_member_row(const Geom& g, long long b
   return base + g.n_special + (long long)r * g.grid_w + c;
 }
 
-// Token row of slot p (0..15) of pooled window w, or -1 outside the grid (or
-// for a window index outside [w_lo, N*nb), which therefore selects nothing).
-__device__ __forceinline__ long long window_slot_row(const Geom& g, int w_lo, int w, int p) {
-  if (w < w_lo || w >= g.n_frames * g.nb) return -1;
+// In-grid token count of pooled window w; 0 for a window index outside
+// [w_lo, N*nb), which therefore selects nothing.
+__device__ __forceinline__ int window_count(const Geom& g, int w_lo, int w) {
+  if (w < w_lo || w >= g.n_frames * g.nb) return 0;
+  const int j = w % g.nb;
+  return min(4, g.grid_h - 4 * (j / g.nbw)) * min(4, g.grid_w - 4 * (j % g.nbw));
+}
+
+// Token row of the i-th in-grid token (0 <= i < window_count) of window w,
+// row-major over the window's in-grid part; token rows fit 31 bits.
+__device__ __forceinline__ int window_token_row(const Geom& g, int w, int i) {
   const int f = w / g.nb, j = w % g.nb;
-  const int r = 4 * (j / g.nbw) + (p >> 2), c = 4 * (j % g.nbw) + (p & 3);
-  if (r >= g.grid_h || c >= g.grid_w) return -1;
-  return (long long)f * g.L + g.n_special + (long long)r * g.grid_w + c;
+  const int r0 = 4 * (j / g.nbw), c0 = 4 * (j % g.nbw);
+  const int cc = min(4, g.grid_w - c0);
+  return f * g.L + g.n_special + (r0 + i / cc) * g.grid_w + c0 + i % cc;
 }
 
 __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) {
@@ -96,59 +106,92 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
   const float c = A.c;
 
   // ---- each wave's selected windows, private LDS stage -----------------------
-  unsigned char* my_stage = smem + wave * kTileStageBytes;
-  const int n_t2 = (A.top_k + 3) / 4;
-  // tiles it = sd * n_t2 + t: block b_wave + sd, windows 4t .. 4t + 3; the
-  // next tile's keys and values are loaded into registers while this one runs
+  unsigned char* my_stage = smem + wave * kWaveLdsBytes;
+  int* my_rows = reinterpret_cast<int*>(my_stage + kTileStageBytes);  // a tile's token rows
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // The next tile to gather: block side gsd (0, 1) from its selected window gwn
+  // on. A tile's keys and values are loaded into registers while the previous
+  // tile runs; tile_n keys of side tile_sd.
+  int gsd = 0, gwn = 0, tile_n = 0, tile_sd = 0;
   u32x4 kreg[4][2], vreg[4][2];
-  bool have[4][2];
-  auto gather = [&](int it) {
-    const int sd = it / n_t2, t = it % n_t2;
-    const long long b = b_wave + sd;
-    const bool bvalid = b < n_qb;
-    const int32_t* sel = A.idx + ((long long)h * n_qb + (bvalid ? b : 0)) * A.top_k;
+  auto gather_next = [&]() -> bool {
+    while (gsd < 2) {
+      const long long b = b_wave + gsd;
+      if (b >= n_qb || gwn >= A.top_k) {
+        ++gsd;
+        gwn = 0;
+        continue;
+      }
+      // lane l looks at selected window gwn + l; the windows whose running
+      // token count stays within 64 (a prefix of the lanes) form the tile
+      const int32_t* sel = A.idx + ((long long)h * n_qb + b) * A.top_k;
+      const int wi = gwn + lane;
+      const int w = wi < A.top_k ? sel[wi] : -1;
+      const int cnt = window_count(g, A.w_lo, w);
+      int incl = cnt;
 #pragma unroll
-    for (int part = 0; part < 4; ++part) {
-      const int u = 2 * ((lane >> 3) + 8 * part);
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const int n_w = __popcll(__ballot(wi < A.top_k && incl <= kTileKeys));  // >= 1
+      const int total = __shfl(incl, n_w - 1);
+      gwn += n_w;
+      if (total == 0) continue;
+      if (lane < n_w) {
+        for (int i = 0; i < cnt; ++i) my_rows[incl - cnt + i] = window_token_row(g, w, i);
+      }
+      wave_sync();
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int wi = 4 * t + ((u + i) >> 4);
-        long long row = -1;
-        if (bvalid && wi < A.top_k) row = window_slot_row(g, A.w_lo, sel[wi], (u + i) & 15);
-        have[part][i] = row >= 0;
-        if (row >= 0) {
-          kreg[part][i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
-          vreg[part][i] = ld16(A.v + row * rs + hoff + (lane & 7) * 8);
-        } else {
-          kreg[part][i] = u32x4{0, 0, 0, 0};
-          vreg[part][i] = u32x4{0, 0, 0, 0};
+      for (int part = 0; part < 4; ++part) {
+        const int u = 2 * ((lane >> 3) + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (u + i < total) {
+            const long long row = my_rows[u + i];
+            kreg[part][i] = ld16(A.k + row * rs + hoff + (lane & 7) * 8);
+            vreg[part][i] = ld16(A.v + row * rs + hoff + (lane & 7) * 8);
+          } else {
+            kreg[part][i] = u32x4{0, 0, 0, 0};
+            vreg[part][i] = u32x4{0, 0, 0, 0};
+          }
         }
       }
+      tile_n = total;
+      tile_sd = gsd;
+      return true;
     }
+    return false;
   };
-  const int n_it = 2 * n_t2;
-  gather(0);
-  for (int it = 0; it < n_it; ++it) {
-    const int sd = it / n_t2;
-    const bool bvalid = b_wave + sd < n_qb;
+  // gather tile t, run tile t - 1 from the stage while tile t's loads are in
+  // flight, then stage tile t
+  int cur_sd = 0, cur_n = 0;
+  bool staged = false;
+  for (;;) {
+    const bool more = gather_next();
+    if (staged) {
+      // the stage is this wave's own: a wave-level wait and barrier suffice
+      wave_sync();
+      st.step(my_stage, off, qB, c, true, side == cur_sd);
+      wave_sync();
+    }
+    if (!more) break;
+    cur_sd = tile_sd;
+    cur_n = tile_n;
 #pragma unroll
     for (int part = 0; part < 4; ++part) {
       const int u = 2 * ((lane >> 3) + 8 * part);
       tile_store_kv_pair(my_stage, u, lane & 7, kreg[part][0], kreg[part][1], vreg[part][0], vreg[part][1]);
       if ((lane & 7) == 0) {
-        tile_bias(my_stage)[u] = have[part][0] ? 0.f : -INFINITY;
-        tile_bias(my_stage)[u + 1] = have[part][1] ? 0.f : -INFINITY;
+        tile_bias(my_stage)[u] = u < cur_n ? 0.f : -INFINITY;
+        tile_bias(my_stage)[u + 1] = u + 1 < cur_n ? 0.f : -INFINITY;
       }
     }
-    if (it + 1 < n_it) gather(it + 1);
-    // the stage is this wave's own: a wave-level wait and barrier suffice
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    st.step(my_stage, off, qB, c, true, side == sd && bvalid);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    staged = true;
   }
 
   st.finish(A.o + (qvalid ? qrow : 0) * rs + hoff,
@@ -201,11 +244,10 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
       for (int s = 0; s < g.n_special; ++s) visit((long long)ff * g.L + s);
   const long long n_qb = (long long)g.n_frames * g.nqb;
   const int32_t* sel = idx + ((long long)h * n_qb + b) * top_k;
-  for (int i = 0; i < top_k; ++i)
-    for (int slot = 0; slot < 16; ++slot) {
-      const long long row = window_slot_row(g, ref ? g.nb : 0, sel[i], slot);
-      if (row >= 0) visit(row);
-    }
+  for (int i = 0; i < top_k; ++i) {
+    const int n = window_count(g, ref ? g.nb : 0, sel[i]);
+    for (int j = 0; j < n; ++j) visit(window_token_row(g, sel[i], j));
+  }
   float* op = o + t * rs + hoff;
   for (int e = 0; e < kHeadDim; ++e) op[e] = acc[e] / l;
   if (lse) lse[t * g.n_heads + h] = m + logf(l);
@@ -279,7 +321,7 @@ hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const voi
   const long long grid = (long long)A.n_wg_per_head * g.n_heads;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gsa_fine_bf16_kernel, dim3((unsigned)grid), dim3(kThreads),
-                     kWaves * kTileStageBytes, stream, A);
+                     kWaves * kWaveLdsBytes, stream, A);
   return hipGetLastError();
 }
 
