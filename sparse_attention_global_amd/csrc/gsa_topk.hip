@@ -68,10 +68,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
 }
 // Lane l's 16 bytes at rsrc + voff land at lds_dst + 16 l (lds_dst wave-uniform);
-// a lane reading past the extent gets zeros.
+// a lane reading past the extent gets zeros. The data is in LDS once vmcnt
+// counts the load done.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, unsigned char* lds_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds_dst, 16,
                                            (int)voff, 0, 0, 0);
+}
+
+// Waits until this wave's direct-to-LDS loads have landed, then meets the other
+// waves: every wave's share of the tile is in LDS. __syncthreads() alone does
+// not suffice: its workgroup-scope fence waits for LDS accesses but not for
+// vector memory loads, so another wave could read a stage before it is filled.
+__device__ __forceinline__ void loads_landed_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); lgkmcnt and expcnt unconstrained
+  __syncthreads();
 }
 
 // planes[h][key] = (hi[64], lo[64]) of k_cmp[key, h, :]: a thread per 8 values.
@@ -386,8 +396,8 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
     const long long u0 = it * kTileN;
     const bool more = it + 1 < n_tiles;
     // tile it has landed in every wave's loads, and every wave is done with
-    // the other stage (the barrier's fence waits for this wave's loads)
-    __syncthreads();
+    // the other stage
+    loads_landed_barrier();
     if (more) tiles.issue(u0 + kTileN, smem + (stage ^ 1) * kStageBytes, wave);
     const unsigned char* hi_p = smem + stage * kStageBytes;
     const unsigned char* lo_p = hi_p + kTileBytes;
@@ -578,9 +588,9 @@ struct ScoreStream {
     for (long long it = 0; it < n_ktiles; it += stride) {
       const long long u0 = it * kTileN;
       const bool more = it + stride < n_ktiles;
-      // tile it has landed (the barrier's fence waits for this wave's loads)
-      // and every wave is done with the other stage
-      __syncthreads();
+      // tile it has landed in every wave's loads, and every wave is done with
+      // the other stage
+      loads_landed_barrier();
       if (more) tiles.issue(u0 + (long long)stride * kTileN, smem + (stage ^ 1) * kStageBytes, wave);
       const unsigned char* hi_p = smem + stage * kStageBytes;
       const unsigned char* lo_p = hi_p + kTileBytes;

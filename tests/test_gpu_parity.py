@@ -605,6 +605,9 @@ def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=
     assert_close(host(out["o_cmp"])[rows], ref["o_cmp"], "bf16", f"{name} o_cmp")
     idx = host(out["idx"]).astype(np.int64)[:, ref["blocks"]]
     check_topk(idx, ref["idx"], ref["ranked"], ref["q_blk"], ref["k_cmp"], f"{name} top-K")
+    again = sga.gsa_select_topk(out["q_blk_f32"], out["k_cmp_f32"], geom, wl.top_k, keep_ref=keep_ref)
+    _sync()
+    assert torch.equal(again, out["idx"]), f"{name} top-K repeat differs"
     # rows whose query block is decided in every head see identical index sets
     dec = decided_blocks(ref["ranked"], wl.top_k).all(axis=0)
     owner = _owner_blocks(geom, rows)
@@ -717,6 +720,17 @@ def test_scene1000_gsa(scene1000):
     assert_close(host(out["o_cmp"])[rows], ref["o_cmp"], "bf16", "scene1000 o_cmp")
     idx = host(out["idx"]).astype(np.int64)[:, ref["blocks"]]
     check_topk(idx, ref["idx"], ref["ranked"], ref["q_blk"], ref["k_cmp"], "scene1000 top-K")
+    # the selection repeats bit for bit at full size, the register path and the
+    # wide one (a tile read before its direct-to-LDS loads landed changed a few
+    # rows per head from call to call)
+    for top_k in (wl.top_k, 128):
+        first = sga.gsa_select_topk(out["q_blk_f32"], out["k_cmp_f32"], geom, top_k)
+        again = sga.gsa_select_topk(out["q_blk_f32"], out["k_cmp_f32"], geom, top_k)
+        _sync()
+        assert torch.equal(first, again), f"scene1000 top-{top_k} repeat differs"
+        if top_k == wl.top_k:
+            assert torch.equal(first, out["idx"]), "scene1000 top-K differs from the layer's"
+        del first, again
     dec = decided_blocks(ref["ranked"], wl.top_k).all(axis=0)
     owner = _owner_blocks(geom, rows)
     pos = {bb: i for i, bb in enumerate(ref["blocks"])}
