@@ -742,6 +742,39 @@ def test_scene1000_gsa(scene1000):
     _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, "scene1000")
 
 
+@pytest.mark.timeout(600)
+def test_scene1000_repeat(scene1000):
+    """Every form and variant twice on the 1000-frame batch: bit-identical.
+    Races between a tile's loads and its readers show only at this size."""
+    wl, geom, q, k, v, probes, _ = scene1000
+    w, b = make_gate(geom.n_heads, 64, seed=1, device=DEV)
+    calls = {
+        "frame": lambda: sga.dense_global_attn(q, k, v, geom, frame_local=True),
+        "subsampled": lambda: sga.subsampled_global_attn(q, k, v, geom, 4, 4),
+        "subsampled log-count": lambda: sga.subsampled_global_attn(q, k, v, geom, 4, 4, mean_log_count=True),
+        "token diagonal": lambda: sga.subsampled_global_attn(q, k, v, geom, 4, 4, mode=2),
+        "gsa top-16": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True),
+        "gsa top-128": lambda: sga.gsa_layer(q, k, v, w, b, geom, 128, keep_intermediates=True),
+        "gsa reference frame": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True,
+                                                     keep_ref=True),
+        "gsa block-level": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True,
+                                                 pooled_q=True),
+        "gsa zero-padded": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True,
+                                                 include_pad=True),
+    }
+    for name, fn in calls.items():
+        _announce(f"scene1000 repeat: {name}")
+        a = fn()
+        c = fn()
+        _sync()
+        if isinstance(a, dict):
+            for key in a:
+                assert torch.equal(a[key], c[key]), f"scene1000 {name}: {key} differs between calls"
+        else:
+            assert torch.equal(a, c), f"scene1000 {name} differs between calls"
+        del a, c
+
+
 @pytest.mark.timeout(1200)
 def test_scene1000_subsampled(scene1000):
     wl, geom, q, k, v, probes, (qh, kh, vh) = scene1000
