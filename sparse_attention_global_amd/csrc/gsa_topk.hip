@@ -441,22 +441,21 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
           const bool c = rvalid && sv > tau;
           if (__any(c)) {
             const int j = (int)u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-            // b(p) = the candidate lands at or before slot p (monotone in p);
-            // walk from the tail so slot p - 1 is read before it is written
+            // Slot p of the new list is the median of (old p - 1, sv, old p):
+            // the list is sorted, so that is old p - 1 when sv goes before it,
+            // sv when it lands at p, old p otherwise. A lane that does not
+            // insert (sv <= tau <= every slot up to top_k - 1) keeps those
+            // slots; an invalid row's lane may change its list, never written.
+            // Walk from the tail so slot p - 1 is read before it is written;
+            // strict compares keep an equal score behind the earlier key.
 #pragma unroll
             for (int p = kRegK - 1; p >= 1; --p) {
-              const bool b = c && sv > lv[p];
-              const bool bp = sv > lv[p - 1];
-              const float tv = bp ? lv[p - 1] : sv;
-              const int tj = bp ? lj[p - 1] : j;
-              lv[p] = b ? tv : lv[p];
-              lj[p] = b ? tj : lj[p];
+              const int tj = sv > lv[p] ? j : lj[p];
+              lj[p] = sv > lv[p - 1] ? lj[p - 1] : tj;
+              lv[p] = __builtin_amdgcn_fmed3f(lv[p - 1], sv, lv[p]);
             }
-            {
-              const bool b = c && sv > lv[0];
-              lv[0] = b ? sv : lv[0];
-              lj[0] = b ? j : lj[0];
-            }
+            lj[0] = sv > lv[0] ? j : lj[0];
+            lv[0] = fmaxf(sv, lv[0]);
             if (FULL) {
               tau = lv[kRegK - 1];
             } else {
