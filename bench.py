@@ -223,6 +223,18 @@ def main():
         # the fine branch's window kernel alone (no always-kept tokens)
         fine_windows_ms = timed(lambda: sga.gsa_sparse_attn(q, k, v, last["idx"], geom, wl.top_k,
                                                             keep_special=False), args.variant_steps)
+        # the gate folded into the fine branch's epilogue (what gsa_layer runs):
+        # against the separate fine and gate calls of the step
+        k_cmp_g, v_cmp_g, _, _ = sga.gsa_compress(q, k, v, geom)
+        o_cmp_g = sga.dense_global_attn(q, k_cmp_g, v_cmp_g, geom, n_keys=N * nb)
+        del k_cmp_g, v_cmp_g
+        t_fg = timed(lambda: sga.gsa_sparse_attn_gated(q, k, v, last["idx"], o_cmp_g, w, b, geom, wl.top_k,
+                                                       ws=ws_fine), args.variant_steps)
+        del o_cmp_g
+        layers["gsa"]["gate_fused_into_fine"] = {
+            "fine_gated_ms": t_fg, "fine_then_gate_ms": per["gsa_fine"] + per["gsa_gate"],
+            "saved_ms": per["gsa_fine"] + per["gsa_gate"] - t_fg,
+            "layer_ms": t_gsa - per["gsa_fine"] - per["gsa_gate"] + t_fg}
         # AVGGT compaction alone (HBM: read K and V, write the compacted set)
         t_cp = timed(lambda: sga.sga_compact(k, v, geom, sh, sw), args.variant_steps)
         cp_bytes = 2 * T * H * d * 2 + 2 * N * (mk + has_mean) * H * d * 2

@@ -179,6 +179,22 @@ sga_status gsa_gate(const sga_geom* geom, const void* q, const void* o_cmp,
                     void* o, void* stream);
 
 /*
+ * GSA fine attention with the gated aggregation folded in (Speed3R section
+ * 2.1, selection branch then gated aggregation; the single fused pass of
+ * Speed3R section 2.2 takes the gate into the selection branch's epilogue):
+ * O = g0 * o_cmp + g1 * (gsa_sparse_attn's result), g as in gsa_gate, with the
+ * fine result taken before it is rounded to the I/O type. Same arguments and
+ * workspace as gsa_sparse_attn, plus o_cmp [T, H, d] (the compressed branch
+ * output), w_gate [H, 2, d] fp32 and b_gate [H, 2] fp32; the fine branch's
+ * output and log-sum-exp are not stored. o must not alias o_cmp (an error).
+ */
+sga_status gsa_sparse_attn_gated(const sga_geom* geom, int32_t block, const void* q,
+                                 const void* k, const void* v, const int32_t* idx,
+                                 int32_t top_k, int32_t keep, const void* o_cmp,
+                                 const float* w_gate, const float* b_gate, void* o,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
  * AVGGT compaction (AVGGT section 2.2): for every frame, its special tokens and
  * its patches with r % stride_h == 0 and c % stride_w == 0 (copied exactly),
  * and -- when any patch is dropped -- one mean K / mean V over the dropped

@@ -27,7 +27,7 @@ SGA_KEEP_SPECIAL = 1
 SGA_KEEP_REF_FRAME = 2
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_compressed_pooled", "gsa_select_topk",
-           "gsa_sparse_attn", "gsa_gate",
+           "gsa_sparse_attn", "gsa_sparse_attn_gated", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
            "sga_version")
 
@@ -55,6 +55,7 @@ def library() -> ctypes.CDLL:
         "gsa_compressed_pooled": [G, I32, P, P, P, P, P, SZ, P],
         "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
+        "gsa_sparse_attn_gated": [G, I32, P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
         "sga_compact": [G, I32, I32, P, P, P, P, P],
         "subsampled_global_attn": [G, I32, I32, I32, I32, P, P, P, P, P, SZ, P],
@@ -279,6 +280,33 @@ def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, b
     return (o, lse) if want_lse else o
 
 
+def gsa_sparse_attn_gated(q, k, v, idx, o_cmp, w_gate, b_gate, geom, top_k: int,
+                          keep_special: bool = True, block: int = 4, ws=None, keep_ref: bool = False):
+    """Fine attention with the gated aggregation folded into its epilogue: the
+    layer output from the compressed branch's o_cmp; see include/sga.h."""
+    T, H, d, N = tokens(geom), geom.n_heads, 64, geom.n_frames
+    nb, nqb = pooled_shape(geom, block)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o_cmp", o_cmp)):
+        _need(t, name, T, H, d, q.dtype)
+    if tuple(idx.shape) != (H, N * nqb, top_k) or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise ValueError(f"idx must be a contiguous int32 tensor of shape {(H, N * nqb, top_k)}")
+    if tuple(w_gate.shape) != (H, 2, d) or w_gate.dtype != torch.float32 or not w_gate.is_contiguous():
+        raise ValueError(f"w_gate must be a contiguous float32 tensor of shape {(H, 2, d)}")
+    if tuple(b_gate.shape) != (H, 2) or b_gate.dtype != torch.float32 or not b_gate.is_contiguous():
+        raise ValueError(f"b_gate must be a contiguous float32 tensor of shape {(H, 2)}")
+    o = torch.empty_like(q)
+    code = _dtype_code(q)
+    g = make_geom(geom, code)
+    ws = _workspace(fine_workspace_bytes(geom, code, keep_special, keep_ref), q.device, ws)
+    _check(library().gsa_sparse_attn_gated(ctypes.byref(g), block, _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                           top_k, keep_flags(keep_special, keep_ref), _ptr(o_cmp),
+                                           _ptr(w_gate), _ptr(b_gate), _ptr(o), _ptr(ws),
+                                           0 if ws is None else ws.numel() * ws.element_size(),
+                                           _stream(q)),
+           "gsa_sparse_attn_gated")
+    return o
+
+
 def gsa_gate(q, o_cmp, o_slc, w_gate, b_gate, geom, out=None):
     """Sigmoid-gated mix of the two GSA branches; see include/sga.h."""
     T, H, d = tokens(geom), geom.n_heads, 64
@@ -349,11 +377,13 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
               keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False,
               pooled_q: bool = False, include_pad: bool = False):
-    """The Global Sparse Attention layer as its five library calls, in order:
-    compress, compressed attention, select, fine attention, gate. ``keep_ref``
-    is the VGGT adaptation: frame 0 kept whole by the fine branch; ``pooled_q``
-    the block-level compressed branch (pooled queries, upsampled);
-    ``include_pad`` the zero-padded pooling."""
+    """The Global Sparse Attention layer: compress, compressed attention,
+    select, then fine attention with the gate folded into its epilogue (with
+    ``keep_intermediates``, fine attention and the gate as separate calls, so
+    that the fine branch's output is kept too). ``keep_ref`` is the VGGT
+    adaptation: frame 0 kept whole by the fine branch; ``pooled_q`` the
+    block-level compressed branch (pooled queries, upsampled); ``include_pad``
+    the zero-padded pooling."""
     N = geom.n_frames
     nb, _ = pooled_shape(geom, block)
     k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block, include_pad=include_pad)
@@ -362,9 +392,10 @@ def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
     else:
         o_cmp = dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
     idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q), keep_ref=keep_ref)
+    if not keep_intermediates:
+        return gsa_sparse_attn_gated(q, k, v, idx, o_cmp, w_gate, b_gate, geom, top_k, keep_special, block,
+                                     keep_ref=keep_ref)
     o_slc = gsa_sparse_attn(q, k, v, idx, geom, top_k, keep_special, block, keep_ref=keep_ref)
     o = gsa_gate(q, o_cmp, o_slc, w_gate, b_gate, geom)
-    if keep_intermediates:
-        return {"k_cmp": k_cmp, "v_cmp": v_cmp, "k_cmp_f32": k32, "q_blk_f32": q32,
-                "o_cmp": o_cmp, "idx": idx, "o_slc": o_slc, "o": o}
-    return o
+    return {"k_cmp": k_cmp, "v_cmp": v_cmp, "k_cmp_f32": k32, "q_blk_f32": q32,
+            "o_cmp": o_cmp, "idx": idx, "o_slc": o_slc, "o": o}

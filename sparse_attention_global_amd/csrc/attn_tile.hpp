@@ -249,6 +249,30 @@ struct WaveAttnState {
       }
     if (lse_ptr != nullptr && hh == 0) *lse_ptr = (m * c + __log2f(l_tot)) * 0.6931471805599453f;
   }
+
+  // As finish, but store g_mix * mix_row + g_self * (this row), the normalised
+  // row taken before rounding (a gated aggregation of two branch outputs).
+  __device__ __forceinline__ void finish_mixed(bf16* orow, const bf16* mix_row, float g_mix, float g_self,
+                                               bool valid) {
+    const int hh = (threadIdx.x & 63) >> 5;
+    const float l_tot = sum_halves(l);
+    const float inv = 1.f / l_tot;
+    if (!valid) return;
+    const float gs = g_self * inv;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hh;
+        const u32x2 mx = *reinterpret_cast<const u32x2*>(mix_row + d0);
+        u32x2 w;
+        w[0] = pack_bf16x2(fmaf(g_mix, lo_bf16(mx[0]), oacc[db][4 * g4 + 0] * gs),
+                           fmaf(g_mix, hi_bf16(mx[0]), oacc[db][4 * g4 + 1] * gs));
+        w[1] = pack_bf16x2(fmaf(g_mix, lo_bf16(mx[1]), oacc[db][4 * g4 + 2] * gs),
+                           fmaf(g_mix, hi_bf16(mx[1]), oacc[db][4 * g4 + 3] * gs));
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+  }
 };
 
 // Q' operand with the softmax scale folded in: bf16(q * c), nearest-even, so

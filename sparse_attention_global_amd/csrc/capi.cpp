@@ -299,9 +299,11 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
                   "gsa_select_topk launch");
 }
 
-sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
-                           const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
-                           void* o_slc, float* lse, void* ws, size_t ws_bytes, void* stream) {
+// The fine branch into `out`; with gate, its gated aggregation with o_cmp.
+static sga_status sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
+                              const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
+                              void* out, float* lse, const sga::FineGate* gate, void* ws,
+                              size_t ws_bytes, void* stream, const char* what) {
   sga::Geom g;
   if (sga_status st = make_geom(geom, &g)) return st;
   if (sga_status st = check_block(block)) return st;
@@ -310,21 +312,23 @@ sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, c
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   REQUIRE_PTR(idx);
-  REQUIRE_PTR(o_slc);
+  const char* out_name = gate ? "o" : "o_slc";
+  if (out == nullptr) return fail(SGA_ERR_INVALID_ARG, "%s must not be null", out_name);
+  if (!aligned16(out)) return fail(SGA_ERR_INVALID_ARG, "%s must be 16-byte aligned", out_name);
   REQUIRE_OPT_PTR(lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf = geom->dtype == SGA_BF16;
   const FineLayout lay = fine_layout(g, bf, keep);
   if (lay.total == 0)
-    return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, o_slc, lse,
-                                         nullptr, nullptr, s),
-                    "gsa_sparse_attn launch");
+    return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, out, lse, nullptr, nullptr,
+                                         gate, s),
+                    what);
   if (ws == nullptr || ws_bytes < lay.total)
     return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.total,
                 ws == nullptr ? 0 : ws_bytes);
   if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
-  // the kept tokens through the dense kernel: o_slc and the log-sum-exp hold
-  // that partial result, which the window kernel continues
+  // the kept tokens through the dense kernel: `out` and the log-sum-exp hold
+  // that partial result, which the window kernel continues (in place)
   unsigned char* w = static_cast<unsigned char*>(ws);
   void* k_s = w;
   void* v_s = w + lay.kv;
@@ -334,16 +338,36 @@ sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, c
   p.q = q;
   p.k = k_s;
   p.v = v_s;
-  p.o = o_slc;
+  p.o = out;
   p.lse = lse_s;
   if (sga_status st = check_fits(p)) return st;
   if (hipError_t e = sga::launch_gather_kept(g, keep, k, v, k_s, v_s, s))
     return from_hip(e, "gsa_sparse_attn (kept tokens) launch");
   if (hipError_t e = sga::launch_flash_bf16(p, flash_ws, s))
     return from_hip(e, "gsa_sparse_attn (kept tokens attention) launch");
-  return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, o_slc, lse,
-                                       static_cast<const sga::bf16*>(o_slc), lse_s, s),
-                  "gsa_sparse_attn launch");
+  return from_hip(sga::launch_gsa_fine(g, bf, q, k, v, idx, top_k, keep, out, lse,
+                                       static_cast<const sga::bf16*>(out), lse_s, gate, s),
+                  what);
+}
+
+sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
+                           const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
+                           void* o_slc, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_attn(geom, block, q, k, v, idx, top_k, keep, o_slc, lse, nullptr, ws, ws_bytes, stream,
+                     "gsa_sparse_attn launch");
+}
+
+sga_status gsa_sparse_attn_gated(const sga_geom* geom, int32_t block, const void* q, const void* k,
+                                 const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
+                                 const void* o_cmp, const float* w_gate, const float* b_gate, void* o,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE_PTR(o_cmp);
+  REQUIRE_PTR(w_gate);
+  if (b_gate == nullptr) return fail(SGA_ERR_INVALID_ARG, "b_gate must not be null");
+  if (o != nullptr && o == o_cmp) return fail(SGA_ERR_INVALID_ARG, "o must not alias o_cmp");
+  const sga::FineGate gate{o_cmp, w_gate, b_gate};
+  return sparse_attn(geom, block, q, k, v, idx, top_k, keep, o, nullptr, &gate, ws, ws_bytes, stream,
+                     "gsa_sparse_attn_gated launch");
 }
 
 sga_status gsa_gate(const sga_geom* geom, const void* q, const void* o_cmp, const void* o_slc,
@@ -486,6 +510,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 60000; }
+int32_t sga_version(void) { return 60100; }
 
 }  // extern "C"

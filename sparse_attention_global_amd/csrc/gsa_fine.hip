@@ -42,6 +42,9 @@ struct FineArgs {
   float* lse;
   const bf16* o_init;     // nullable: partial result each query starts from
   const float* lse_init;  // its log-sum-exp (natural log of the scaled logits)
+  const bf16* o_cmp;      // nullable: gate the result with the compressed branch
+  const float* w_gate;    // [H, 2, d] with o_cmp
+  const float* b_gate;    // [H, 2]
   Geom g;
   int top_k;
   int w_lo;          // first pooled window that may contribute (nb when frame 0 is kept whole)
@@ -194,8 +197,33 @@ __global__ __launch_bounds__(kThreads, 2) void gsa_fine_bf16_kernel(FineArgs A) 
     staged = true;
   }
 
-  st.finish(A.o + (qvalid ? qrow : 0) * rs + hoff,
-            A.lse ? A.lse + (qvalid ? qrow : 0) * g.n_heads + h : nullptr, qvalid, c);
+  if (A.o_cmp == nullptr) {
+    st.finish(A.o + (qvalid ? qrow : 0) * rs + hoff,
+              A.lse ? A.lse + (qvalid ? qrow : 0) * g.n_heads + h : nullptr, qvalid, c);
+    return;
+  }
+  // gated aggregation (the gate of gsa_gate.hip) on the unrounded fine row:
+  // the gate logits q . W[h]^T from the lane's 32 query values (d = 16 ks +
+  // 8 hh + e, the Q operand), the other 32 in lane l ^ 32
+  const int hh = lane >> 5;
+  const float* w0 = A.w_gate + (long long)h * 2 * kHeadDim;
+  const float* w1 = w0 + kHeadDim;
+  float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = 16 * ks + 8 * hh + 2 * jj;
+      const float a0 = lo_bf16(qB[ks][jj]), a1 = hi_bf16(qB[ks][jj]);
+      z0 = fmaf(a1, w0[d + 1], fmaf(a0, w0[d], z0));
+      z1 = fmaf(a1, w1[d + 1], fmaf(a0, w1[d], z1));
+    }
+  z0 += __shfl_xor(z0, 32);
+  z1 += __shfl_xor(z1, 32);
+  const float g0 = 1.f / (1.f + expf(-(z0 + A.b_gate[2 * h])));
+  const float g1 = 1.f / (1.f + expf(-(z1 + A.b_gate[2 * h + 1])));
+  const long long r = qvalid ? qrow : 0;
+  st.finish_mixed(A.o + r * rs + hoff, A.o_cmp + r * rs + hoff, g0, g1, qvalid);
 }
 
 // fp32 path: one thread per (query, head), exact online softmax over the same
@@ -206,7 +234,10 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
                                                           const int32_t* __restrict__ idx,
                                                           int top_k, int keep,
                                                           float* __restrict__ o,
-                                                          float* __restrict__ lse) {
+                                                          float* __restrict__ lse,
+                                                          const float* __restrict__ o_cmp,
+                                                          const float* __restrict__ w_gate,
+                                                          const float* __restrict__ b_gate) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
   if (t >= g.T) return;
@@ -249,6 +280,19 @@ __global__ __launch_bounds__(64) void gsa_fine_f32_kernel(Geom g, const float* _
     for (int j = 0; j < n; ++j) visit(window_token_row(g, sel[i], j));
   }
   float* op = o + t * rs + hoff;
+  if (o_cmp != nullptr) {  // gated aggregation (the gate of gsa_gate.hip)
+    const float* w0 = w_gate + (long long)h * 2 * kHeadDim;
+    float z0 = 0.f, z1 = 0.f;
+    for (int e = 0; e < kHeadDim; ++e) {
+      z0 = fmaf(qp[e], w0[e], z0);
+      z1 = fmaf(qp[e], w0[kHeadDim + e], z1);
+    }
+    const float g0 = 1.f / (1.f + expf(-(z0 + b_gate[2 * h])));
+    const float g1 = 1.f / (1.f + expf(-(z1 + b_gate[2 * h + 1])));
+    const float* cp = o_cmp + t * rs + hoff;
+    for (int e = 0; e < kHeadDim; ++e) op[e] = g0 * cp[e] + g1 * (acc[e] / l);
+    return;
+  }
   for (int e = 0; e < kHeadDim; ++e) op[e] = acc[e] / l;
   if (lse) lse[t * g.n_heads + h] = m + logf(l);
 }
@@ -292,13 +336,17 @@ hipError_t launch_gather_kept(const Geom& g, int keep, const void* k, const void
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
                            const void* v, const int32_t* idx, int top_k, int keep,
                            void* o, float* lse, const bf16* o_init, const float* lse_init,
-                           hipStream_t stream) {
+                           const FineGate* gate, hipStream_t stream) {
+  if (gate != nullptr && (gate->o_cmp == nullptr || gate->w == nullptr || gate->b == nullptr))
+    return hipErrorInvalidValue;
   if (!is_bf16) {
     dim3 grid((unsigned)((g.T + 63) / 64), (unsigned)g.n_heads);
     hipLaunchKernelGGL(gsa_fine_f32_kernel, grid, dim3(64), 0, stream, g,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), idx, top_k, keep,
-                       static_cast<float*>(o), lse);
+                       static_cast<float*>(o), lse,
+                       gate ? static_cast<const float*>(gate->o_cmp) : nullptr,
+                       gate ? gate->w : nullptr, gate ? gate->b : nullptr);
     return hipGetLastError();
   }
   // bf16: the kept tokens come in through o_init / lse_init only
@@ -315,6 +363,11 @@ hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const voi
   A.w_lo = (keep & kKeepRefFrame) ? g.nb : 0;
   A.o_init = o_init;
   A.lse_init = lse_init;
+  if (gate != nullptr) {
+    A.o_cmp = static_cast<const bf16*>(gate->o_cmp);
+    A.w_gate = gate->w;
+    A.b_gate = gate->b;
+  }
   A.c = kLog2e / sqrtf((float)kHeadDim);
   const long long n_qb = (long long)g.n_frames * g.nqb;
   A.n_wg_per_head = (int)((n_qb + kBlocksPerWG - 1) / kBlocksPerWG);

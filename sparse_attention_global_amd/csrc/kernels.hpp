@@ -84,10 +84,18 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
 // that partial result (the attention over the kept tokens, normalised, and its
 // log-sum-exp) and the selected windows continue it. With kKeepRefFrame a
 // window of frame 0 in idx contributes nothing (frame 0 is already counted).
+// gate (nullable): write g0 * o_cmp + g1 * (the fine result) instead, with
+// g = sigmoid(q . w[h]^T + b[h]) (the gated aggregation of launch_gsa_gate);
+// o must not alias o_cmp.
+struct FineGate {
+  const void* o_cmp;
+  const float* w;
+  const float* b;
+};
 hipError_t launch_gsa_fine(const Geom& g, bool is_bf16, const void* q, const void* k,
                            const void* v, const int32_t* idx, int top_k, int keep,
                            void* o, float* lse, const bf16* o_init, const float* lse_init,
-                           hipStream_t stream);
+                           const FineGate* gate, hipStream_t stream);
 // The kept tokens' keys and values, gathered contiguously ([kept_rows, H, d],
 // in kept_rows order) for the dense kernel (gsa_fine.hip).
 hipError_t launch_gather_kept(const Geom& g, int keep, const void* k, const void* v, void* k_s,

@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 60000
+    assert library().sga_version() == 60100
 
 
 def geom(**kw):
@@ -108,6 +108,27 @@ def test_gsa_calls_reject_bad_arguments():
     assert L.gsa_sparse_attn(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 101, 3, FAKE, None, None, 0,
                              None) == INVALID
     assert L.gsa_gate(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
+    # the gated fine entry point: the gate's inputs, and an output that would
+    # overwrite o_cmp while it is read
+    OTHER = ctypes.c_void_p(0x20000)
+    gated = L.gsa_sparse_attn_gated
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, None, FAKE, FAKE, OTHER, None, 0,
+                 None) == INVALID
+    assert "o_cmp" in last_error()
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, None, OTHER, None, 0,
+                 None) == INVALID
+    assert "b_gate" in last_error()
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, FAKE, FAKE, None, 0,
+                 None) == INVALID
+    assert "alias" in last_error()
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, FAKE, None, None, 0,
+                 None) == INVALID
+    assert "o must not be null" in last_error()
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 4, FAKE, FAKE, FAKE, OTHER, None, 0,
+                 None) == INVALID
+    assert "keep" in last_error()
+    assert gated(ctypes.byref(g), 4, FAKE, FAKE, FAKE, FAKE, 16, 1, FAKE, FAKE, FAKE, OTHER, None, 0,
+                 None) == WORKSPACE
 
 
 def test_subsampled_rejects_bad_arguments():

@@ -127,6 +127,11 @@ def test_small_every_op(geom, top_k, stride):
     o_g = sga.gsa_gate(q, o_cmp, o_slc, w, b, geom)
     _sync()
     assert_close(host(o_g), oracle.gate(qh, host(o_cmp), host(o_slc), host(w), host(b)), dt, "gate")
+    # the gate folded into the fine branch: oracle fine result (same index
+    # sets), GPU compressed output (shared input)
+    o_gf = sga.gsa_sparse_attn_gated(q, k, v, idx_in, o_cmp, w, b, geom, top_k)
+    _sync()
+    assert_close(host(o_gf), oracle.gate(qh, host(o_cmp), r_slc, host(w), host(b)), dt, "gate fused into fine")
 
     # the whole layer, on rows whose blocks are decided in every head
     out = sga.gsa_layer(q, k, v, w, b, geom, top_k)
@@ -580,9 +585,11 @@ def _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, top_k, name, keep_
     idx_mix[:, torch.from_numpy(ref["blocks"]).to(DEV)] = torch.from_numpy(ref["idx"]).to(DEV)
     o_slc = sga.gsa_sparse_attn(q, k, v, idx_mix, geom, top_k, keep_ref=keep_ref)
     o = sga.gsa_gate(q, out["o_cmp"], o_slc, w, b, geom)
+    o_fused = sga.gsa_sparse_attn_gated(q, k, v, idx_mix, out["o_cmp"], w, b, geom, top_k, keep_ref=keep_ref)
     _sync()
     assert_close(host(o_slc)[rows], ref["o_slc"], "bf16", f"{name} o_slc (oracle sets, all rows)")
     assert_close(host(o)[rows], ref["o"], "bf16", f"{name} gsa layer (oracle sets, all rows)")
+    assert_close(host(o_fused)[rows], ref["o"], "bf16", f"{name} gate fused into fine (oracle sets, all rows)")
 
 
 def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=False):
@@ -617,6 +624,11 @@ def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=
     if keep.any():  # (with close block scores no sampled row may be decided in all 16 heads)
         assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", f"{name} o_slc")
         assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer")
+        # the layer as one returns it (the gate folded into the fine branch)
+        o_fused = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_ref=keep_ref, pooled_q=pooled_q,
+                                include_pad=include_pad)
+        _sync()
+        assert_close(host(o_fused)[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer (fused gate)")
     else:
         assert include_pad, "only the zero-padded pooling leaves no sampled row decided here"
     _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, name, keep_ref)
