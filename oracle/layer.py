@@ -58,6 +58,11 @@ R19 the grid zero-padded to whole windows before the 4x4 average (the
     alternative to R4): a window that overhangs the grid sums its in-grid
     tokens and divides by 16. The mean queries of the query blocks (R2, R3)
     stay over their tokens.
+R20 the block score read as probabilities (the alternative to R2): the mean
+    over the query block's tokens of their compressed-branch softmax
+    probabilities, p_tj = exp(s_tj - lse_t) with lse_t over all N*nb pooled
+    keys (with R15 frame 0's blocks still normalise, they only do not
+    compete); ties and order as R6.
 
 Arrays are ``[rows, H, d]`` of any float dtype; every computation widens them
 to fp64 first.
@@ -74,7 +79,8 @@ __all__ = [
     "attend", "attend_union", "dense_attention", "frame_attention", "window_table",
     "query_block_table", "compress", "pooled_queries", "compressed_attention",
     "compressed_attention_pooled",
-    "block_scores", "select_topk", "fine_key_rows", "fine_attention", "gate",
+    "block_scores", "select_topk", "probability_block_scores", "select_topk_probability",
+    "fine_key_rows", "fine_attention", "gate",
     "gsa_layer", "subsample_plan", "sga_compact", "subsampled_attention",
     "head_map",
 ]
@@ -309,6 +315,69 @@ def block_scores(q_blk, k_cmp):
     return np.einsum("bhd,jhd->hbj", qb, kc) / math.sqrt(d)
 
 
+def _topk_rows(s, top_k: int, first: int):
+    """Top-K of each row of s [n, nk] (larger first, ties to the lower column,
+    R6): (idx [n, K] int32 ascending, offset by ``first``; ranked [n, K+1]
+    fp64, the K+1 best in rank order, -inf padded)."""
+    n, nk = s.shape
+    m = min(top_k + 1, nk)
+    idx = np.empty((n, top_k), dtype=np.int32)
+    ranked = np.full((n, top_k + 1), -np.inf)
+    # every key ranked within the first m scores at least the m-th largest
+    thr = np.partition(s, nk - m, axis=1)[:, nk - m]
+    for i in range(n):
+        row = s[i]
+        cand = np.nonzero(row >= thr[i])[0]
+        order = sorted(cand.tolist(), key=lambda j: (-row[j], j))
+        idx[i] = first + np.sort(np.array(order[:top_k], dtype=np.int32))
+        ranked[i, :m] = row[order[:m]]
+    return idx, ranked
+
+
+def probability_block_scores(q, k_cmp, geom, block: int, blocks, first: int = 0, workers=None):
+    """R20 block scores of the query blocks ``blocks``: for every pooled key j
+    >= ``first``, the mean over the block's tokens t of their compressed
+    softmax probability exp(s_tj - lse_t), s_tj = q_t . k~_j / sqrt(d), lse_t
+    over all pooled keys ([Speed3R-ja] section 2.1: the compressed branch's
+    attention in the compressed space guides the selection). Returns fp64
+    [H, len(blocks), N*nb - first]."""
+    qq = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cmp, dtype=np.float64)
+    H, d = qq.shape[1], qq.shape[2]
+    qbt = query_block_table(geom, block)
+    out = np.empty((H, len(blocks), kc.shape[0] - first))
+
+    def one_head(h):
+        kh = kc[:, h, :]
+        for i, bb in enumerate(blocks):
+            s = (qq[qbt[bb], h, :] @ kh.T) / math.sqrt(d)      # [tokens, all pooled keys]
+            mx = s.max(axis=1, keepdims=True)
+            lse = mx + np.log(np.exp(s - mx).sum(axis=1, keepdims=True))
+            out[h, i] = np.exp(s - lse).mean(axis=0)[first:]
+
+    head_map(one_head, H, workers)
+    return out
+
+
+def select_topk_probability(q, k_cmp, geom, top_k: int, block: int, blocks, first: int = 0,
+                            workers=None):
+    """Top-K pooled blocks per (head, query block in ``blocks``) under R20
+    scores, the selection rule of R6. Returns (idx [H, n, K] int32 ascending,
+    global; ranked [H, n, K+1] fp64 = the natural log of the K+1 best scores in
+    rank order, so that gaps between them read as relative)."""
+    sc = probability_block_scores(q, k_cmp, geom, block, blocks, first=first, workers=workers)
+    H, n, nk = sc.shape
+    if not 1 <= top_k <= nk:
+        raise ValueError("top_k must lie in [1, number of competing pooled keys]")
+    idx = np.empty((H, n, top_k), dtype=np.int32)
+    ranked = np.empty((H, n, top_k + 1))
+    for h in range(H):
+        idx[h], r = _topk_rows(sc[h], top_k, first)
+        with np.errstate(divide="ignore"):
+            ranked[h] = np.log(r)
+    return idx, ranked
+
+
 def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None, first: int = 0):
     """Top-K pooled blocks per (head, query block) from the compressed scores
     ([Speed3R-ja] section 2.1, selection branch, first bullet; [Speed3R-it]
@@ -326,20 +395,12 @@ def select_topk(q_blk, k_cmp, top_k: int, chunk: int = 64, workers=None, first: 
         raise ValueError("top_k must lie in [1, number of competing pooled keys]")
     idx = np.empty((H, n, top_k), dtype=np.int32)
     ranked = np.full((H, n, top_k + 1), -np.inf)
-    m = min(top_k + 1, nk)
 
     def one_head(h):
         kh = kc[:, h, :]
         for a in range(0, n, chunk):
             s = (qb[a:a + chunk, h, :] @ kh.T) / math.sqrt(d)
-            # every key ranked within the first m scores at least the m-th largest
-            thr = np.partition(s, nk - m, axis=1)[:, nk - m]
-            for i in range(s.shape[0]):
-                row = s[i]
-                cand = np.nonzero(row >= thr[i])[0]
-                order = sorted(cand.tolist(), key=lambda j: (-row[j], j))
-                idx[h, a + i] = first + np.sort(np.array(order[:top_k], dtype=np.int32))
-                ranked[h, a + i, :m] = row[order[:m]]
+            idx[h, a:a + chunk], ranked[h, a:a + chunk] = _topk_rows(s, top_k, first)
 
     head_map(one_head, H, workers)
     return idx, ranked
@@ -418,12 +479,13 @@ def gate(q, o_cmp, o_slc, w, b):
 
 def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
               keep_special=True, workers=None, keep_ref=False, pooled_q=False,
-              include_pad=False):
+              include_pad=False, probability_scores=False):
     """The whole Global Sparse Attention layer for the query rows ``rows``:
     pool, compressed branch, block scores + top-K, fine branch, gate.
     ``keep_ref`` is the VGGT adaptation (R15); ``pooled_q`` the block-level
-    compressed branch (R18); ``include_pad`` the zero-padded pooling (R19).
-    Returns a dict with every intermediate."""
+    compressed branch (R18); ``include_pad`` the zero-padded pooling (R19);
+    ``probability_scores`` the probability-mean block score (R20; ``ranked``
+    then holds log scores). Returns a dict with every intermediate."""
     T = q.shape[0]
     rows = _rows(rows, T)
     k_cmp, v_cmp = compress(k, v, geom, block, include_pad=include_pad)
@@ -438,7 +500,11 @@ def gsa_layer(q, k, v, geom, w, b, top_k: int, block: int = 4, rows=None,
     need = np.unique(owner[rows])
     q_blk = pooled_queries(q, geom, block, blocks=need)
     first = len(window_table(_one_frame(geom), block)) if keep_ref else 0
-    idx_need, ranked = select_topk(q_blk, k_cmp, top_k, workers=workers, first=first)
+    if probability_scores:
+        idx_need, ranked = select_topk_probability(q, k_cmp, geom, top_k, block, need, first=first,
+                                                   workers=workers)
+    else:
+        idx_need, ranked = select_topk(q_blk, k_cmp, top_k, workers=workers, first=first)
     H = q.shape[1]
     idx_full = np.zeros((H, len(qbt), top_k), dtype=np.int32)
     idx_full[:, need] = idx_need

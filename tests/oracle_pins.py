@@ -623,4 +623,78 @@ def pin_pool_zero_padded():
     for a, b in zip(L.compress(k, v, G_FULL, 4, include_pad=True), L.compress(k, v, G_FULL, 4)):
         _close(a, b, 1e-15)
 
+# ------------------------------------------------- probability block score (R20)
+
+def _prob_inputs(seed):
+    q, k, v = _qkv(G_SMALL, seed)
+    kc, _ = L.compress(k, v, G_SMALL, 4)
+    return q, kc
+
+
+def pin_probability_scores_sum_to_one():
+    """Each token's compressed probabilities sum to one, so a block's mean of
+    them does too: summed over every pooled key, each block's scores are 1."""
+    q, kc = _prob_inputs(30)
+    blocks = list(range(G_SMALL.n_frames * 5))
+    sc = L.probability_block_scores(q, kc, G_SMALL, 4, blocks)
+    _close(sc.sum(axis=2), np.ones(sc.shape[:2]), 1e-13)
+    assert (sc > 0).all()
+
+
+def pin_probability_scores_brute_force():
+    """R20 against a plain loop over tokens and keys (tiny input): softmax of
+    each token's scaled logits over all pooled keys, averaged over the
+    block's valid tokens; with the first F keys out of the competition the
+    returned scores are the same numbers for the other keys."""
+    q, kc = _prob_inputs(31)
+    H, d = q.shape[1], q.shape[2]
+    qbt = L.query_block_table(G_SMALL, 4)
+    blocks = [0, 3, 4, 9, 14]          # full, edge and corner windows, a specials block
+    F = 4
+    sc = L.probability_block_scores(q, kc, G_SMALL, 4, blocks)
+    scf = L.probability_block_scores(q, kc, G_SMALL, 4, blocks, first=F)
+    for h in range(H):
+        for i, bb in enumerate(blocks):
+            rows = list(qbt[bb])
+            want = [0.0] * kc.shape[0]
+            for t in rows:
+                logits = [sum(q[t, h, e] * kc[j, h, e] for e in range(d)) / math.sqrt(d)
+                          for j in range(kc.shape[0])]
+                z = sum(math.exp(x) for x in logits)
+                for j in range(kc.shape[0]):
+                    want[j] += math.exp(logits[j]) / z / len(rows)
+            _close(sc[h, i], want, 1e-12)
+            _close(scf[h, i], want[F:], 1e-12)
+
+
+def pin_probability_equal_queries_is_logit_order():
+    """When every token of a block has the same query, its probability-mean
+    scores are that query's softmax over the pooled keys -- a monotone map of
+    the R2 logits -- so both readings select the same blocks, in the same rank
+    order, and the log scores differ from the logits by one constant."""
+    q, kc = _prob_inputs(32)
+    qbt = L.query_block_table(G_SMALL, 4)
+    for members in qbt:               # each block's tokens take its first token's query
+        q[members] = q[members[0]]
+    blocks = list(range(len(qbt)))
+    q_blk = L.pooled_queries(q, G_SMALL, 4, blocks=blocks)
+    for K in (1, 3, 6):
+        i_p, r_p = L.select_topk_probability(q, kc, G_SMALL, K, 4, blocks)
+        i_l, r_l = L.select_topk(q_blk, kc, K)
+        assert np.array_equal(i_p, i_l), K
+        diff = r_p - r_l
+        _close(diff, np.broadcast_to(diff[..., :1], diff.shape), 1e-12)
+
+
+def pin_probability_key_shift_invariance():
+    """Adding one vector c to every pooled key shifts each token's logits by the
+    constant q.c/sqrt(d): its softmax, and so the scores, stay the same."""
+    q, kc = _prob_inputs(33)
+    blocks = [0, 2, 5, 9]
+    c = _rng(34).standard_normal((1,) + kc.shape[1:]) * 2.0
+    a = L.probability_block_scores(q, kc, G_SMALL, 4, blocks)
+    b = L.probability_block_scores(q, kc + c, G_SMALL, 4, blocks)
+    _close(a, b, 1e-10)
+
+
 ALL_PINS = [obj for name, obj in sorted(globals().items()) if name.startswith("pin_")]

@@ -25,10 +25,10 @@ MUTATIONS = [
      "rows.append(f * L + S + c * gh + r)"),
     ("no_special_query_block", "query_block_table", "        if S:\n", "        if False:\n"),
     ("block_score_unscaled", "block_scores", "/ math.sqrt(d)", ""),
-    ("topk_ties_high", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (-row[j], -j)"),
-    ("topk_rank_order", "select_topk", "np.sort(np.array(order[:top_k], dtype=np.int32))",
+    ("topk_ties_high", "_topk_rows", "key=lambda j: (-row[j], j)", "key=lambda j: (-row[j], -j)"),
+    ("topk_rank_order", "_topk_rows", "np.sort(np.array(order[:top_k], dtype=np.int32))",
      "np.array(order[:top_k], dtype=np.int32)"),
-    ("topk_smallest", "select_topk", "key=lambda j: (-row[j], j)", "key=lambda j: (row[j], j)"),
+    ("topk_smallest", "_topk_rows", "key=lambda j: (-row[j], j)", "key=lambda j: (row[j], j)"),
     ("fine_drops_specials", "fine_attention", "if use_spec:", "if False:"),
     ("ref_specials_twice", "fine_attention", "f0 = 1 if keep_ref else 0", "f0 = 0"),
     ("ref_frame_dropped", "fine_attention", "            if keep_ref:\n", "            if False:\n"),
@@ -36,7 +36,7 @@ MUTATIONS = [
      "ref = np.arange(geom.n_special if keep_ref else 0, L if keep_ref else 0)"),
     ("ref_rows_specials_twice", "fine_key_rows", "f0 = 1 if keep_ref else 0", "f0 = 0"),
     ("topk_first_ignored", "select_topk", "dtype=np.float64)[first:]", "dtype=np.float64)"),
-    ("topk_first_local_index", "select_topk", "first + np.sort(", "np.sort("),
+    ("topk_first_local_index", "_topk_rows", "first + np.sort(", "np.sort("),
     ("gsa_ref_selects_frame0", "gsa_layer", "if keep_ref else 0\n", "if False else 0\n"),
     ("gate_swapped", "gate", "g[..., 0:1] * np.asarray(o_cmp", "g[..., 1:2] * np.asarray(o_cmp"),
     ("gate_no_bias", "gate", " + np.asarray(b, np.float64)", ""),
@@ -64,6 +64,20 @@ MUTATIONS = [
      "diag = np.ones(len(rows), dtype=bool)"),
     ("diag_no_log_count", "_subsampled_token_diagonal", "bias_c[m - 1::m] = math.log(len(dropped))",
      "pass"),
+    ("prob_no_lse", "probability_block_scores", "out[h, i] = np.exp(s - lse).mean(axis=0)[first:]",
+     "out[h, i] = np.exp(s).mean(axis=0)[first:]"),
+    ("prob_sum_not_mean", "probability_block_scores", "out[h, i] = np.exp(s - lse).mean(axis=0)[first:]",
+     "out[h, i] = np.exp(s - lse).sum(axis=0)[first:]"),
+    ("prob_max_not_mean", "probability_block_scores", "out[h, i] = np.exp(s - lse).mean(axis=0)[first:]",
+     "out[h, i] = np.exp(s - lse).max(axis=0)[first:]"),
+    ("prob_lse_over_competing", "probability_block_scores",
+     "s = (qq[qbt[bb], h, :] @ kh.T) / math.sqrt(d)",
+     "s = (qq[qbt[bb], h, :] @ kh[first:].T) / math.sqrt(d); s = np.concatenate([np.full((s.shape[0], first), -np.inf), s], axis=1)"),
+    ("prob_no_scale", "probability_block_scores", "s = (qq[qbt[bb], h, :] @ kh.T) / math.sqrt(d)",
+     "s = (qq[qbt[bb], h, :] @ kh.T)"),
+    ("prob_first_token_only", "probability_block_scores", "s = (qq[qbt[bb], h, :] @ kh.T) / math.sqrt(d)",
+     "s = (qq[qbt[bb][:1], h, :] @ kh.T) / math.sqrt(d)"),
+    ("prob_ranked_not_log", "select_topk_probability", "ranked[h] = np.log(r)", "ranked[h] = r"),
     ("diag_own_frame_masked", "_subsampled_token_diagonal", "s_c = (qc @ ckh.T) * scale + bias_c",
      "s_c = (qc @ ckh.T) * scale + bias_c; s_c[:, :m] = -np.inf"),
 ]
