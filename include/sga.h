@@ -147,6 +147,28 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
                            void* stream);
 
 /*
+ * GSA block selection with probability-mean block scores (the alternative
+ * reading of the selection branch's block score, Speed3R section 2.1: the
+ * attention of the compressed branch guides the selection): the score of
+ * pooled key j for query block b is the mean over b's tokens t of
+ * exp(s_tj - lse_t), s_tj = q[t,h] . k_cmp[j,h] / sqrt(d), lse_t the log of
+ * sum_j' exp(s_tj') over all N*nb pooled keys (also with SGA_KEEP_REF_FRAME,
+ * where only j >= nb compete). The top_k best j are kept, ties going to the
+ * lower j.
+ * q: [T, H, d] bf16 (the token queries; bf16 only, else SGA_ERR_UNSUPPORTED).
+ * k_cmp_f32, keep, idx, score: as gsa_select_topk; score holds the mean
+ *   probabilities. 1 <= top_k <= min(competing keys, 16); above 16:
+ *   SGA_ERR_UNSUPPORTED.
+ * ws: sga_workspace_size(geom, SGA_OP_TOPK_PROB, top_k, keep, &bytes) bytes:
+ *   the key planes of gsa_select_topk, then every token's log-sum-exp (fp32
+ *   [T, H]).
+ */
+sga_status gsa_select_topk_probability(const sga_geom* geom, int32_t block, const void* q,
+                                       const float* k_cmp_f32, int32_t top_k, int32_t keep,
+                                       int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                                       void* stream);
+
+/*
  * GSA fine attention (Speed3R section 2.1, selection branch): each query of
  * query block b attends to the in-grid tokens of the pooled blocks listed in
  * idx[h, b, :] plus what `keep` (SGA_KEEP_* flags) always keeps: every special
@@ -224,14 +246,16 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
                                   const void* k, const void* v, void* o, void* ws,
                                   size_t ws_bytes, void* stream);
 
-enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4, SGA_OP_POOLED = 5 };
+enum { SGA_OP_SUBSAMPLED = 1, SGA_OP_DENSE = 2, SGA_OP_FINE = 3, SGA_OP_TOPK = 4, SGA_OP_POOLED = 5,
+       SGA_OP_TOPK_PROB = 6 };
 
 /* Workspace bytes an operation needs (0 if none). SGA_OP_DENSE: param0 =
  * n_keys (0 = T), param1 = frame_local. SGA_OP_SUBSAMPLED: param0, param1 =
  * stride_h, stride_w (covers every mode). SGA_OP_FINE: param0 = keep (the
  * SGA_KEEP_* flags of gsa_sparse_attn), param1 unused (0). SGA_OP_TOPK:
- * param0 = top_k, param1 = keep (as gsa_select_topk). SGA_OP_POOLED
- * (gsa_compressed_pooled): param0 = param1 = 0. */
+ * param0 = top_k, param1 = keep (as gsa_select_topk); SGA_OP_TOPK_PROB the
+ * same for gsa_select_topk_probability. SGA_OP_POOLED (gsa_compressed_pooled):
+ * param0 = param1 = 0. */
 sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0,
                               int32_t param1, size_t* bytes);
 

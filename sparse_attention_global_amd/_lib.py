@@ -23,10 +23,12 @@ SGA_OP_DENSE = 2
 SGA_OP_FINE = 3
 SGA_OP_TOPK = 4
 SGA_OP_POOLED = 5
+SGA_OP_TOPK_PROB = 6
 SGA_KEEP_SPECIAL = 1
 SGA_KEEP_REF_FRAME = 2
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_compressed_pooled", "gsa_select_topk",
+           "gsa_select_topk_probability",
            "gsa_sparse_attn", "gsa_sparse_attn_gated", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
            "sga_version")
@@ -54,6 +56,7 @@ def library() -> ctypes.CDLL:
         "gsa_compress": [G, I32, I32, P, P, P, P, P, P, P, P],
         "gsa_compressed_pooled": [G, I32, P, P, P, P, P, SZ, P],
         "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
+        "gsa_select_topk_probability": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn_gated": [G, I32, P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
         "gsa_gate": [G, P, P, P, P, P, P, P],
@@ -255,6 +258,35 @@ def fine_workspace_bytes(geom, dtype_code: int, keep_special: bool = True,
     return n.value
 
 
+def topk_prob_workspace_bytes(geom, top_k: int, keep_ref: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    g = make_geom(geom, SGA_BF16)
+    _check(library().sga_workspace_size(ctypes.byref(g), SGA_OP_TOPK_PROB, top_k,
+                                        keep_flags(False, keep_ref), ctypes.byref(n)),
+           "sga_workspace_size")
+    return n.value
+
+
+def gsa_select_topk_probability(q, k_cmp_f32, geom, top_k: int, block: int = 4, want_score: bool = False,
+                                keep_ref: bool = False, ws=None):
+    """Top-K pooled blocks per (head, query block) by the mean over the block's
+    tokens of their compressed softmax probabilities (bf16 q, top_k <= 16);
+    see include/sga.h."""
+    T, H, d, N = tokens(geom), geom.n_heads, 64, geom.n_frames
+    nb, nqb = pooled_shape(geom, block)
+    _need(q, "q", T, H, d, torch.bfloat16)
+    _need(k_cmp_f32, "k_cmp_f32", N * nb, H, d, torch.float32)
+    idx = torch.empty((H, N * nqb, top_k), dtype=torch.int32, device=q.device)
+    score = torch.empty((H, N * nqb, top_k), dtype=torch.float32, device=q.device) if want_score else None
+    g = make_geom(geom, SGA_BF16)
+    ws = _workspace(topk_prob_workspace_bytes(geom, top_k, keep_ref), q.device, ws)
+    _check(library().gsa_select_topk_probability(ctypes.byref(g), block, _ptr(q), _ptr(k_cmp_f32), top_k,
+                                                 keep_flags(False, keep_ref), _ptr(idx), _ptr(score),
+                                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(q)),
+           "gsa_select_topk_probability")
+    return (idx, score) if want_score else idx
+
+
 def gsa_sparse_attn(q, k, v, idx, geom, top_k: int, keep_special: bool = True, block: int = 4,
                     want_lse: bool = False, ws=None, keep_ref: bool = False):
     """Fine attention over the selected blocks (+ all special tokens, + frame 0
@@ -376,14 +408,15 @@ def subsampled_global_attn(q, k, v, geom, s_h: int, s_w: int, mode: int = 0,
 
 def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
               keep_special: bool = True, keep_intermediates: bool = False, keep_ref: bool = False,
-              pooled_q: bool = False, include_pad: bool = False):
+              pooled_q: bool = False, include_pad: bool = False, probability_scores: bool = False):
     """The Global Sparse Attention layer: compress, compressed attention,
     select, then fine attention with the gate folded into its epilogue (with
     ``keep_intermediates``, fine attention and the gate as separate calls, so
     that the fine branch's output is kept too). ``keep_ref`` is the VGGT
     adaptation: frame 0 kept whole by the fine branch; ``pooled_q`` the
     block-level compressed branch (pooled queries, upsampled); ``include_pad``
-    the zero-padded pooling."""
+    the zero-padded pooling; ``probability_scores`` selects by the mean of the
+    block's tokens' compressed probabilities instead of their mean logit."""
     N = geom.n_frames
     nb, _ = pooled_shape(geom, block)
     k_cmp, v_cmp, k32, q32 = gsa_compress(q, k, v, geom, block, include_pad=include_pad)
@@ -391,7 +424,10 @@ def gsa_layer(q, k, v, w_gate, b_gate, geom, top_k: int, block: int = 4,
         o_cmp = gsa_compressed_pooled(q32, k_cmp, v_cmp, geom, block)
     else:
         o_cmp = dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
-    idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q), keep_ref=keep_ref)
+    if probability_scores:
+        idx = gsa_select_topk_probability(q, k32, geom, top_k, block, keep_ref=keep_ref)
+    else:
+        idx = gsa_select_topk(q32, k32, geom, top_k, block, dtype_code=_dtype_code(q), keep_ref=keep_ref)
     if not keep_intermediates:
         return gsa_sparse_attn_gated(q, k, v, idx, o_cmp, w_gate, b_gate, geom, top_k, keep_special, block,
                                      keep_ref=keep_ref)

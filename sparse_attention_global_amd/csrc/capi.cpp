@@ -105,6 +105,15 @@ sga_status check_topk(const sga::Geom& g, int32_t top_k, int32_t keep) {
   return SGA_OK;
 }
 
+// The probability-mean selection: bf16 only, top_k <= 16 (register lists).
+sga_status check_topk_prob(const sga_geom* geom, const sga::Geom& g, int32_t top_k, int32_t keep) {
+  if (sga_status st = check_topk(g, top_k, keep)) return st;
+  if (geom->dtype != SGA_BF16)
+    return fail(SGA_ERR_UNSUPPORTED, "probability-mean block scores take bf16 queries only");
+  if (top_k > 16) return fail(SGA_ERR_UNSUPPORTED, "probability-mean block scores: top_k %d > 16", top_k);
+  return SGA_OK;
+}
+
 // Rows per frame of the compacted set (kept part) and whether a mean row exists.
 void compact_shape(const sga::Geom& g, int s_h, int s_w, int* mk, int* has_mean, int* n_drop) {
   const int kh = (g.grid_h + s_h - 1) / s_h, kw = (g.grid_w + s_w - 1) / s_w;
@@ -350,6 +359,26 @@ static sga_status sparse_attn(const sga_geom* geom, int32_t block, const void* q
                   what);
 }
 
+sga_status gsa_select_topk_probability(const sga_geom* geom, int32_t block, const void* q,
+                                       const float* k_cmp_f32, int32_t top_k, int32_t keep, int32_t* idx,
+                                       float* score, void* ws, size_t ws_bytes, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  if (sga_status st = check_topk_prob(geom, g, top_k, keep)) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cmp_f32);
+  REQUIRE_PTR(idx);
+  REQUIRE_OPT_PTR(score);
+  const size_t need = sga::gsa_topk_prob_workspace(g);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws == nullptr ? 0 : ws_bytes);
+  if (!aligned16(ws)) return fail(SGA_ERR_INVALID_ARG, "ws must be 16-byte aligned");
+  return from_hip(sga::launch_gsa_topk_prob(g, q, k_cmp_f32, top_k, first_candidate(g, keep), idx, score, ws,
+                                            static_cast<hipStream_t>(stream)),
+                  "gsa_select_topk_probability launch");
+}
+
 sga_status gsa_sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
                            const void* v, const int32_t* idx, int32_t top_k, int32_t keep,
                            void* o_slc, float* lse, void* ws, size_t ws_bytes, void* stream) {
@@ -418,6 +447,11 @@ sga_status sga_workspace_size(const sga_geom* geom, int32_t op, int32_t param0, 
   if (op == SGA_OP_TOPK) {
     if (sga_status st = check_topk(g, param0, param1)) return st;
     *bytes = sga::gsa_topk_workspace(g, param0);
+    return SGA_OK;
+  }
+  if (op == SGA_OP_TOPK_PROB) {
+    if (sga_status st = check_topk_prob(geom, g, param0, param1)) return st;
+    *bytes = sga::gsa_topk_prob_workspace(g);
     return SGA_OK;
   }
   if (op == SGA_OP_FINE) {
@@ -510,6 +544,6 @@ sga_status subsampled_global_attn(const sga_geom* geom, int32_t stride_h, int32_
 
 const char* sga_last_error(void) { return g_last_error.c_str(); }
 
-int32_t sga_version(void) { return 60100; }
+int32_t sga_version(void) { return 60200; }
 
 }  // extern "C"

@@ -881,6 +881,244 @@ int resident_workgroups(const void* kernel, int threads, size_t lds) {
   return per_cu * n_cu;
 }
 
+// ---------------------------------------------------------------------------
+// Probability-mean block scores (the block score read as probabilities: the
+// mean over a query block's tokens of their compressed-branch softmax
+// probabilities, Speed3R technical summary section 2.1), top_k <= 16.
+//
+// 1. gsa_token_lse_kernel: every token's log-sum-exp over all pooled keys. The
+//    token's bf16 query times 1/8 is exact in bf16, so two bf16 products per
+//    operand chunk (q k_hi + q k_lo) give fp32-accurate logits; the layout is
+//    the selection's (S^T = K Q^T, a lane per token, its 32 of every 64 keys),
+//    with an online log-sum-exp per lane, merged with the partner lane.
+// 2. gsa_topk_prob_kernel: a wave takes two query blocks, their member tokens
+//    as the 32 MFMA rows (S = Q K^T: a lane per key, 8 rows of each block in
+//    each half-wave). A block's probability sum for a key is the lane's 8
+//    terms plus its partner's; the lane of the first half keeps the first
+//    block's register list (the keys = its lane mod 32), the second half the
+//    second block's, and at the end the 32 lists of a block are sorted
+//    together.
+// ---------------------------------------------------------------------------
+
+// Token row of member m (0..15) of query block b, or -1 for an empty slot (a
+// window's out-of-grid position, a specials block's slot >= S, b past the end).
+__device__ __forceinline__ long long member_row(const Geom& g, long long b, int m) {
+  if (b >= (long long)g.n_frames * g.nqb) return -1;
+  const int f = (int)(b / g.nqb), j = (int)(b % g.nqb);
+  const long long base = (long long)f * g.L;
+  if (j == g.nb) return m < g.n_special ? base + m : -1;
+  const int r = 4 * (j / g.nbw) + (m >> 2), c = 4 * (j % g.nbw) + (m & 3);
+  if (r >= g.grid_h || c >= g.grid_w) return -1;
+  return base + g.n_special + (long long)r * g.grid_w + c;
+}
+
+// The 8 values d = 16 ks + 8 hh .. + 7 of a bf16 row times 1/8 (exact), or 0.
+__device__ __forceinline__ void load_row_eighth(const bf16* row, bool valid, int hh, u32x4 (&x)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 w = valid ? ld16(row + hh * 8 + ks * 16) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[ks][j] = pack_bf16x2(lo_bf16(w[j]) * 0.125f, hi_bf16(w[j]) * 0.125f);
+  }
+}
+
+// lse2[t, h] = log2 sum_j exp2(s_tj log2 e), s_tj = q_t . k~_j / 8, over all
+// n_total pooled keys; 128 tokens of one head per workgroup.
+__global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf16* __restrict__ q,
+                                                              const void* __restrict__ planes,
+                                                              long long n_total, int n_rowtiles,
+                                                              float* __restrict__ lse2) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int h = blockIdx.x / n_rowtiles;
+  const long long row0 = (long long)(blockIdx.x % n_rowtiles) * 128;
+  const long long rs = (long long)g.n_heads * kHeadDim;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  const long long t = row0 + wave * 32 + li;
+  const bool tvalid = t < g.T;
+  u32x4 qb[4];
+  load_row_eighth(q + (tvalid ? t : 0) * rs + (long long)h * kHeadDim, tvalid, hh, qb);
+
+  PlaneTiles tiles;
+  tiles.init(planes, n_total, h, 0, n_total, tid);
+  float m2 = -INFINITY, l = 0.f;  // running max (log2 units) and sum over this lane's keys
+  const long long n_tiles = (n_total + kTileN - 1) / kTileN;
+  tiles.issue(0, smem, wave);
+  for (long long it = 0; it < n_tiles; ++it) {
+    const int stage = (int)(it & 1);
+    const long long u0 = it * kTileN;
+    const bool more = it + 1 < n_tiles;
+    loads_landed_barrier();
+    if (more) tiles.issue(u0 + kTileN, smem + (stage ^ 1) * kStageBytes, wave);
+    const unsigned char* hi_p = smem + stage * kStageBytes;
+    const unsigned char* lo_p = hi_p + kTileBytes;
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 ah = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
+        const u32x4 al = ld16(lo_p + t_off(kb * 32 + li, 2 * ks + hh));
+        acc = mfma32(al, qb[ks], acc);
+        acc = mfma32(ah, qb[ks], acc);
+      }
+      s[kb] = acc;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = s[kb][i] * kLog2e;
+        if (!more) {  // the last tile: keys past the end take no part
+          const long long j = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (j >= n_total) x = -INFINITY;
+        }
+        s[kb][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    if (mx > m2) {
+      l *= __builtin_amdgcn_exp2f(m2 - mx);
+      m2 = mx;
+    }
+    // (a lane whose keys so far all lie past the end keeps l = 0: -inf - -inf
+    // would be NaN)
+    const float base = m2 > -INFINITY ? m2 : 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(s[kb][i] - base);
+  }
+  const float mo = __shfl_xor(m2, 32), lo = __shfl_xor(l, 32);
+  const float mm = fmaxf(m2, mo);
+  const float lt = l * __builtin_amdgcn_exp2f(m2 - mm) + lo * __builtin_amdgcn_exp2f(mo - mm);
+  if (tvalid && hh == 0) lse2[t * g.n_heads + h] = mm + __log2f(lt);
+}
+
+constexpr int kProbBlocksPerWG = 8;  // two query blocks per wave
+
+template <bool FULL>  // FULL: top_k == kRegK
+__global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf16* __restrict__ q,
+                                                              const void* __restrict__ planes,
+                                                              long long n_total, long long n_cand, int j0,
+                                                              int top_k, const float* __restrict__ lse2,
+                                                              int n_wg_per_head, int32_t* __restrict__ idx,
+                                                              float* __restrict__ score) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int h = blockIdx.x / n_wg_per_head;
+  const long long wg = blockIdx.x % n_wg_per_head;
+  const long long n_qb = (long long)g.n_frames * g.nqb;
+  const long long rs = (long long)g.n_heads * kHeadDim;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  const long long b_wave = wg * kProbBlocksPerWG + 2 * wave;
+
+  // A operand: MFMA row li = member li % 16 of block b_wave + li / 16
+  u32x4 qa[4];
+  {
+    const long long r = member_row(g, b_wave + (li >> 4), li & 15);
+    load_row_eighth(q + (r >= 0 ? r : 0) * rs + (long long)h * kHeadDim, r >= 0, hh, qa);
+  }
+  // this lane's 16 result rows m = 8 (i / 4) + 4 hh + i % 4 (i < 8: block
+  // b_wave, else b_wave + 1) take -lse2 of their token, -inf for an empty slot
+  float nl[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = 8 * (i >> 2) + 4 * hh + (i & 3);
+    const long long r = member_row(g, b_wave + (m >> 4), m & 15);
+    nl[i] = r >= 0 ? -lse2[r * g.n_heads + h] : -INFINITY;
+  }
+  // the block whose list this lane keeps (first half: b_wave), its token count
+  int cnt = 0;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) cnt += member_row(g, b_wave + hh, m) >= 0 ? 1 : 0;
+  const float inv = cnt > 0 ? 1.f / (float)cnt : 0.f;
+
+  PlaneTiles tiles;
+  tiles.init(planes, n_total, h, j0, n_cand, tid);
+  float lv[kRegK];
+  int lj[kRegK];
+#pragma unroll
+  for (int p = 0; p < kRegK; ++p) { lv[p] = -INFINITY; lj[p] = 0x7fffffff; }
+  float tau = -INFINITY;
+  const int kth = top_k - 1;
+
+  const long long n_tiles = (n_cand + kTileN - 1) / kTileN;
+  tiles.issue(0, smem, wave);
+  for (long long it = 0; it < n_tiles; ++it) {
+    const int stage = (int)(it & 1);
+    const long long u0 = it * kTileN;
+    const bool more = it + 1 < n_tiles;
+    loads_landed_barrier();
+    if (more) tiles.issue(u0 + kTileN, smem + (stage ^ 1) * kStageBytes, wave);
+    const unsigned char* hi_p = smem + stage * kStageBytes;
+    const unsigned char* lo_p = hi_p + kTileBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 bh = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
+        const u32x4 bl = ld16(lo_p + t_off(kb * 32 + li, 2 * ks + hh));
+        acc = mfma32(qa[ks], bl, acc);
+        acc = mfma32(qa[ks], bh, acc);
+      }
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p0 += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nl[i]));
+#pragma unroll
+      for (int i = 8; i < 16; ++i) p1 += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nl[i]));
+      p0 += __shfl_xor(p0, 32);
+      p1 += __shfl_xor(p1, 32);
+      const int j = (int)u0 + kb * 32 + li;
+      const float sv = (j < n_cand) ? (hh == 0 ? p0 : p1) * inv : -INFINITY;
+      if (__any(sv > tau)) {
+        // the median insertion network of gsa_topk_reg_kernel
+#pragma unroll
+        for (int p = kRegK - 1; p >= 1; --p) {
+          const int tj = sv > lv[p] ? j : lj[p];
+          lj[p] = sv > lv[p - 1] ? lj[p - 1] : tj;
+          lv[p] = __builtin_amdgcn_fmed3f(lv[p - 1], sv, lv[p]);
+        }
+        lj[0] = sv > lv[0] ? j : lj[0];
+        lv[0] = fmaxf(sv, lv[0]);
+        if (FULL) {
+          tau = lv[kRegK - 1];
+        } else {
+          float t = lv[0];
+#pragma unroll
+          for (int p = 1; p < kRegK; ++p) t = (p == kth) ? lv[p] : t;
+          tau = t;
+        }
+      }
+    }
+  }
+
+  // ---- each block's 32 lists (512 keys) sorted together -----------------------
+  __syncthreads();  // every wave is done with the stages: they hold the lists now
+  uint64_t* lists = reinterpret_cast<uint64_t*>(smem) + wave * 2 * 32 * kRegK;
+  uint64_t* sel_lds = reinterpret_cast<uint64_t*>(smem + 2 * kStageBytes) + wave * kRegK;
+#pragma unroll
+  for (int p = 0; p < kRegK; ++p) lists[hh * 32 * kRegK + li * kRegK + p] = order_key(lv[p], lj[p]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const long long b = b_wave + side;
+    if (b >= n_qb) break;  // wave-uniform
+    int32_t* ip = idx + ((long long)h * n_qb + b) * top_k;
+    float* sp = score ? score + ((long long)h * n_qb + b) * top_k : nullptr;
+    select_block<8>(lists + side * 32 * kRegK, 32 * kRegK, 0, top_k, lane, sel_lds, j0, ip, sp);
+  }
+}
+
 }  // namespace
 
 static size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -889,6 +1127,50 @@ static size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 // selection then the per-workgroup key buffers, the bounds and the flags.
 static size_t planes_bytes(const Geom& g) {
   return round_up256((size_t)g.n_frames * g.nb * g.n_heads * kPlaneRowBytes);
+}
+
+size_t gsa_topk_prob_workspace(const Geom& g) {
+  return planes_bytes(g) + round_up256((size_t)g.T * g.n_heads * sizeof(float));
+}
+
+hipError_t launch_gsa_topk_prob(const Geom& g, const void* q, const float* k_cmp, int top_k, int first,
+                                int32_t* idx, float* score, void* ws, hipStream_t stream) {
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const long long n_total = (long long)g.n_frames * g.nb;
+  const long long n_cand = n_total - first;
+  if (top_k < 1 || top_k > kRegK || top_k > n_cand) return hipErrorInvalidValue;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  void* planes = w;
+  float* lse2 = reinterpret_cast<float*>(w + planes_bytes(g));
+  {
+    const long long n = n_total * g.n_heads * 8;
+    const long long blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cmp, n_total,
+                       g.n_heads, static_cast<u32x4*>(planes));
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  const bf16* qb = static_cast<const bf16*>(q);
+  {
+    const int n_rowtiles = (int)((g.T + 127) / 128);
+    const long long grid = (long long)n_rowtiles * g.n_heads;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gsa_token_lse_kernel, dim3((unsigned)grid), dim3(256), 2 * kStageBytes, stream, g, qb,
+                       planes, n_total, n_rowtiles, lse2);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  const int n_wg = (int)((n_rows + kProbBlocksPerWG - 1) / kProbBlocksPerWG);
+  const long long grid = (long long)n_wg * g.n_heads;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const size_t lds = 2 * kStageBytes + 4 * kRegK * sizeof(uint64_t);
+  if (top_k == kRegK) {
+    hipLaunchKernelGGL(gsa_topk_prob_kernel<true>, dim3((unsigned)grid), dim3(256), lds, stream, g, qb, planes,
+                       n_total, n_cand, first, top_k, lse2, n_wg, idx, score);
+  } else {
+    hipLaunchKernelGGL(gsa_topk_prob_kernel<false>, dim3((unsigned)grid), dim3(256), lds, stream, g, qb, planes,
+                       n_total, n_cand, first, top_k, lse2, n_wg, idx, score);
+  }
+  return hipGetLastError();
 }
 
 size_t gsa_topk_workspace(const Geom& g, int top_k) {

@@ -75,6 +75,14 @@ inline long long kept_rows(const Geom& g, int keep) {
 // (the wide selection's per-workgroup key buffers and overflow flags; none
 // for top_k <= 16).
 size_t gsa_topk_workspace(const Geom& g, int top_k);
+// Probability-mean block scores (gsa_topk.hip): top-K (<= 16) per (head, query
+// block) of the mean over the block's tokens of their compressed softmax
+// probabilities (q bf16 [T, H, d]); keys j >= first compete, every pooled key
+// normalises. ws: gsa_topk_prob_workspace(g) bytes (key planes, then the
+// tokens' log-sum-exp).
+size_t gsa_topk_prob_workspace(const Geom& g);
+hipError_t launch_gsa_topk_prob(const Geom& g, const void* q, const float* k_cmp, int top_k, int first,
+                                int32_t* idx, float* score, void* ws, hipStream_t stream);
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
                            int first, int32_t* idx, float* score, void* ws, hipStream_t stream);
 

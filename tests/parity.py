@@ -52,9 +52,11 @@ def assert_close(got, ref, dtype: str, what: str):
         assert rel <= F32_REL_L2, (what, max_abs, rel)
 
 
-def check_topk(idx_gpu, idx_ref, ranked_ref, q_blk_ref, k_cmp_ref, what: str):
+def check_topk(idx_gpu, idx_ref, ranked_ref, q_blk_ref, k_cmp_ref, what: str, score_of=None):
     """idx_gpu / idx_ref [H, n, K] (same rows); ranked_ref [H, n, K+1] oracle
-    scores in rank order; q_blk_ref [n, H, d], k_cmp_ref [nk, H, d] fp64."""
+    scores in rank order; q_blk_ref [n, H, d], k_cmp_ref [nk, H, d] fp64.
+    score_of(h, b, picks) gives the oracle scores of picked keys in ranked_ref's
+    units (default: the pooled query's logit)."""
     idx_gpu = np.asarray(idx_gpu)
     H, n, K = idx_ref.shape
     kth = ranked_ref[:, :, K - 1]
@@ -67,11 +69,14 @@ def check_topk(idx_gpu, idx_ref, ranked_ref, q_blk_ref, k_cmp_ref, what: str):
     assert not bad.any(), f"{what}: {int(bad.sum())} decided rows differ"
     # each row is a set of distinct ascending indices
     assert np.all(np.diff(idx_gpu, axis=2) > 0), f"{what}: rows not strictly ascending"
-    d = q_blk_ref.shape[-1]
+    d = q_blk_ref.shape[-1] if score_of is None else None
     for h in range(H):
         und = np.nonzero(~decided[h])[0]
         for b in und:
-            s = k_cmp_ref[idx_gpu[h, b], h, :] @ q_blk_ref[b, h, :] / math.sqrt(d)
+            if score_of is not None:
+                s = score_of(h, b, idx_gpu[h, b])
+            else:
+                s = k_cmp_ref[idx_gpu[h, b], h, :] @ q_blk_ref[b, h, :] / math.sqrt(d)
             assert np.all(s >= kth[h, b] - TOPK_GAP), (what, h, b)
     return decided
 

@@ -32,7 +32,7 @@ def test_header_functions_are_exported():
 
 
 def test_version():
-    assert library().sga_version() == 60100
+    assert library().sga_version() == 60200
 
 
 def geom(**kw):
@@ -237,6 +237,28 @@ def test_topk_workspace():
     # a missing workspace is reported before anything is launched
     assert library().gsa_select_topk(ctypes.byref(g), 4, FAKE, FAKE, 17, 0, FAKE, None, None, 0,
                                      None) == WORKSPACE
+    assert "workspace" in last_error()
+
+
+def test_topk_probability_workspace_and_checks():
+    g = geom(n_frames=256)
+    T = 256 * (5 + 37 * 37)
+    planes = r256(256 * 100 * 16 * 256)
+    # the key planes, then an fp32 log-sum-exp per (token, head)
+    assert _ws(g, 6, 16, 0) == (OK, planes + r256(T * 16 * 4))
+    assert _ws(g, 6, 16, 2) == (OK, planes + r256(T * 16 * 4))
+    assert _ws(g, 6, 17, 0)[0] == UNSUPPORTED
+    assert _ws(g, 6, 0, 0)[0] == INVALID
+    assert _ws(geom(n_frames=4, dtype=1), 6, 4, 0)[0] == UNSUPPORTED
+    L = library()
+    sel = L.gsa_select_topk_probability
+    assert sel(ctypes.byref(g), 4, FAKE, FAKE, 17, 0, FAKE, None, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert "16" in last_error()
+    assert sel(ctypes.byref(geom(n_frames=4, dtype=1)), 4, FAKE, FAKE, 4, 0, FAKE, None, FAKE, 1 << 40,
+               None) == UNSUPPORTED
+    assert "bf16" in last_error()
+    assert sel(ctypes.byref(g), 4, None, FAKE, 16, 0, FAKE, None, FAKE, 1 << 40, None) == INVALID
+    assert sel(ctypes.byref(g), 4, FAKE, FAKE, 16, 0, FAKE, None, None, 0, None) == WORKSPACE
     assert "workspace" in last_error()
 
 

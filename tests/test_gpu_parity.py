@@ -592,27 +592,37 @@ def _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, top_k, name, keep_
     assert_close(host(o_fused)[rows], ref["o"], "bf16", f"{name} gate fused into fine (oracle sets, all rows)")
 
 
-def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=False):
+def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=False,
+               probability_scores=False):
     wl, geom, q, k, v = _workload_inputs(name)
     w, b = make_gate(geom.n_heads, 64, seed=1, device=DEV)
     rows = sample_rows(geom.n_tokens, rows_cap or wl.check_rows, seed=1).numpy()
     _announce(f"{name} GSA layer (reference frame kept: {keep_ref}, block-level compressed: "
               f"{pooled_q}), {len(rows)} rows")
     out = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_intermediates=True, keep_ref=keep_ref,
-                        pooled_q=pooled_q, include_pad=include_pad)
+                        pooled_q=pooled_q, include_pad=include_pad, probability_scores=probability_scores)
     _sync()
     qh, kh, vh = host(q), host(k), host(v)
     W = oracle_workers()
     ref = oracle.gsa_layer(qh, kh, vh, geom, host(w), host(b), wl.top_k, rows=rows, workers=W,
-                           keep_ref=keep_ref, pooled_q=pooled_q, include_pad=include_pad)
+                           keep_ref=keep_ref, pooled_q=pooled_q, include_pad=include_pad,
+                           probability_scores=probability_scores)
     assert_close(host(out["k_cmp"]), ref["k_cmp"], "bf16", f"{name} k_cmp")
     assert_close(host(out["v_cmp"]), ref["v_cmp"], "bf16", f"{name} v_cmp")
     assert_close(host(out["k_cmp_f32"]), ref["k_cmp"], "f32", f"{name} k_cmp_f32")
     assert_close(host(out["q_blk_f32"])[ref["blocks"]], ref["q_blk"], "f32", f"{name} q_blk_f32")
     assert_close(host(out["o_cmp"])[rows], ref["o_cmp"], "bf16", f"{name} o_cmp")
     idx = host(out["idx"]).astype(np.int64)[:, ref["blocks"]]
-    check_topk(idx, ref["idx"], ref["ranked"], ref["q_blk"], ref["k_cmp"], f"{name} top-K")
-    again = sga.gsa_select_topk(out["q_blk_f32"], out["k_cmp_f32"], geom, wl.top_k, keep_ref=keep_ref)
+    score_of = None
+    if probability_scores:
+        first = _nb(geom) if keep_ref else 0
+        psc = oracle.probability_block_scores(qh, ref["k_cmp"], geom, 4, ref["blocks"], first=first, workers=W)
+        score_of = lambda h, bi, picks: np.log(psc[h, bi, picks - first])  # noqa: E731
+    check_topk(idx, ref["idx"], ref["ranked"], ref["q_blk"], ref["k_cmp"], f"{name} top-K", score_of=score_of)
+    if probability_scores:
+        again = sga.gsa_select_topk_probability(q, out["k_cmp_f32"], geom, wl.top_k, keep_ref=keep_ref)
+    else:
+        again = sga.gsa_select_topk(out["q_blk_f32"], out["k_cmp_f32"], geom, wl.top_k, keep_ref=keep_ref)
     _sync()
     assert torch.equal(again, out["idx"]), f"{name} top-K repeat differs"
     # rows whose query block is decided in every head see identical index sets
@@ -626,7 +636,7 @@ def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=
         assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer")
         # the layer as one returns it (the gate folded into the fine branch)
         o_fused = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_ref=keep_ref, pooled_q=pooled_q,
-                                include_pad=include_pad)
+                                include_pad=include_pad, probability_scores=probability_scores)
         _sync()
         assert_close(host(o_fused)[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer (fused gate)")
     else:
@@ -679,6 +689,51 @@ def _sga_check(name, rows_cap=None):
                  f"{name} subsampled token diagonal")
     assert_close(host(of)[rows], oracle.frame_attention(qh, kh, vh, geom, rows=rows), "bf16",
                  f"{name} frame")
+
+
+PROB_GEOMS = [
+    pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), id="ragged"),
+    pytest.param(Geometry(1, 1, 5, 7, 1, 64, "bf16"), id="one-frame"),
+    pytest.param(Geometry(5, 0, 1, 1, 1, 64, "bf16"), id="1x1-grid"),
+    pytest.param(Geometry(2, 16, 3, 5, 2, 64, "bf16"), id="16-specials"),
+    pytest.param(Geometry(6, 5, 37, 37, 2, 64, "bf16"), id="scene"),
+]
+
+
+@pytest.mark.parametrize("geom", PROB_GEOMS)
+def test_probability_block_scores(geom):
+    """Selection by probability-mean block scores against the oracle on every
+    query block, for several widths and with the reference frame kept."""
+    _announce(f"probability-mean selection {geom}")
+    q, k, v = make_qkv(geom, seed=41, device=DEV, distribution="scene")
+    _, _, k32, _ = sga.gsa_compress(q, k, v, geom)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    rkc, _ = oracle.compress(kh, vh, geom, 4)
+    N, nb = geom.n_frames, _nb(geom)
+    blocks = list(range(N * _nqb(geom)))
+    for keep_ref in ((False, True) if N >= 2 else (False,)):
+        first = nb if keep_ref else 0
+        n_cand = N * nb - first
+        psc = oracle.probability_block_scores(qh, rkc, geom, 4, blocks, first=first)
+        for top_k in sorted({1, min(5, n_cand), min(16, n_cand)}):
+            idx, sc = sga.gsa_select_topk_probability(q, k32, geom, top_k, want_score=True, keep_ref=keep_ref)
+            again = sga.gsa_select_topk_probability(q, k32, geom, top_k, keep_ref=keep_ref)
+            _sync()
+            assert torch.equal(idx, again)
+            ridx, ranked = oracle.select_topk_probability(qh, rkc, geom, top_k, 4, blocks, first=first)
+            idx_h = host(idx).astype(np.int64)
+            check_topk(idx_h, ridx, ranked, None, None, f"probability top-{top_k} keep_ref={keep_ref}",
+                       score_of=lambda h, bi, picks: np.log(psc[h, bi, picks - first]))
+            # the scores the kernel reports are the oracle's for its picks
+            want = np.take_along_axis(psc, idx_h - first, axis=2)
+            rel = np.max(np.abs(host(sc) - want) / want)
+            print(f"[parity] probability scores top-{top_k}: max rel err {rel:.2e}", flush=True)
+            assert rel < 1e-4
+
+
+def test_gsa128_probability_scores():
+    _gsa_check("gsa128", rows_cap=1024, probability_scores=True)
 
 
 @pytest.mark.timeout(900)
