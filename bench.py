@@ -97,7 +97,7 @@ def main():
 
     last = {}
 
-    def gsa_chain(ev, i, top_k, keep_ref, ws_f, pooled_q=False, include_pad=False):
+    def gsa_chain(ev, i, top_k, keep_ref, ws_f, pooled_q=False, include_pad=False, prob=False):
         """The five GSA calls, an event recorded after each."""
         k_cmp, v_cmp, k32, q32 = sga.gsa_compress(q, k, v, geom, include_pad=include_pad)
         ev[i].record(); i += 1
@@ -106,7 +106,10 @@ def main():
         else:
             o_cmp = sga.dense_global_attn(q, k_cmp, v_cmp, geom, n_keys=N * nb)
         ev[i].record(); i += 1
-        idx = sga.gsa_select_topk(q32, k32, geom, top_k, keep_ref=keep_ref)
+        if prob:
+            idx = sga.gsa_select_topk_probability(q, k32, geom, top_k, keep_ref=keep_ref)
+        else:
+            idx = sga.gsa_select_topk(q32, k32, geom, top_k, keep_ref=keep_ref)
         ev[i].record(); i += 1
         o_slc = sga.gsa_sparse_attn(q, k, v, idx, geom, top_k, ws=ws_f, keep_ref=keep_ref)
         ev[i].record(); i += 1
@@ -179,10 +182,12 @@ def main():
     }
     if args.variant_steps > 0:
         layers["gsa_variants"] = {}
-        for vname, vk, vref, vpool, vpad in (("vggt_reference_frame", wl.top_k, True, False, False),
-                                             ("top128", 128, False, False, False),
-                                             ("block_level_compressed", wl.top_k, False, True, False),
-                                             ("zero_padded_pooling", wl.top_k, False, False, True)):
+        for vname, vk, vref, vpool, vpad, vprob in (
+                ("vggt_reference_frame", wl.top_k, True, False, False, False),
+                ("top128", 128, False, False, False, False),
+                ("block_level_compressed", wl.top_k, False, True, False, False),
+                ("zero_padded_pooling", wl.top_k, False, False, True, False),
+                ("probability_mean_block_score", wl.top_k, False, False, False, True)):
             ws_v = torch.empty(sga.fine_workspace_bytes(geom, sga.SGA_BF16, True, vref),
                                dtype=torch.uint8, device=dev)
             gnames = [n for n in names if n.startswith("gsa_")]
@@ -190,7 +195,7 @@ def main():
             for rep in range(1 + args.variant_steps):  # the first pass is untimed
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(gnames) + 1)]
                 ev[0].record()
-                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v, vpool, vpad)
+                _, vidx = gsa_chain(ev, 1, vk, vref, ws_v, vpool, vpad, vprob)
                 torch.cuda.synchronize()
                 if rep:
                     for j, n in enumerate(gnames):
@@ -198,10 +203,10 @@ def main():
             t_v = sum(vper.values())
             layers["gsa_variants"][vname] = {
                 "top_k": vk, "reference_frame_kept": vref, "block_level_compressed": vpool,
-                "zero_padded_pooling": vpad, "ms": t_v,
+                "zero_padded_pooling": vpad, "probability_mean_block_score": vprob, "ms": t_v,
                 "tokens_per_s": T / t_v * 1e3, "speedup_vs_dense": per["dense"] / t_v,
                 "kernels_ms": {n[4:]: vper[n] for n in gnames},
-                "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref, pooled_q=vpool)}
+                "kernels_roofline": gsa_rooflines(geom, vper, vidx, keep_ref=vref, pooled_q=vpool, prob=vprob)}
             del ws_v, vidx
             print(f"[bench] variant {vname}: {t_v:.1f} ms", file=sys.stderr, flush=True)
 
@@ -338,7 +343,7 @@ def avggt_schedule(sga, torch, make_qkv, geom1000, wl, dev, timed, seed):
     return out
 
 
-def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False, fine_windows_ms=None):
+def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False, fine_windows_ms=None, prob=False):
     """Per-step roofline of the GSA kernels from their timed durations:
     algorithmic bytes (HBM-bound steps) or flop (MFMA steps) per call. With
     ``keep_ref`` frame 0 is attended whole and its blocks do not compete.
@@ -364,8 +369,11 @@ def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False, fine_windows_m
     out = {}
     pool_bytes = 3 * T * H * d * 2 + N * nb * H * d * (2 + 2 + 4) + N * nqb * H * d * 4
     gate_bytes = 4 * T * H * d * 2
+    # top-K: one product per block score; with probability-mean scores one per
+    # token logit, twice (the log-sum-exp over all pooled keys, then the sums)
+    topk_flop = (2.0 * d * T * (N * nb + n_cand) * H) if prob else 2.0 * d * (N * nqb) * n_cand * H
     flops = {"compressed": 4.0 * (N * nqb if pooled_q else T) * N * nb * d * H,
-             "topk": 2.0 * d * (N * nqb) * n_cand * H,  # one product per score
+             "topk": topk_flop,
              "fine": 4.0 * d * pairs}
     for name, nbytes in (("pool", pool_bytes), ("gate", gate_bytes)):
         gbs = nbytes / (per["gsa_" + name] * 1e-3) / 1e9
@@ -373,9 +381,11 @@ def gsa_rooflines(geom, per, idx, keep_ref=False, pooled_q=False, fine_windows_m
     for name, fl in flops.items():
         tf = fl / (per["gsa_" + name] * 1e-3) / 1e12
         out[name] = {"bound": "mfma", "tflops": tf, "frac": tf / PEAK_BF16_TFLOPS, "flop": fl}
-    # the scores run as three bf16 products (hi*hi + hi*lo + lo*hi) for fp32 accuracy
-    out["topk"]["executed_flop"] = 3 * flops["topk"]
-    out["topk"]["executed_tflops"] = 3 * out["topk"]["tflops"]
+    # the scores run as three bf16 products (hi*hi + hi*lo + lo*hi) for fp32
+    # accuracy; token logits as two (the bf16 query times hi and lo)
+    mult = 2 if prob else 3
+    out["topk"]["executed_flop"] = mult * flops["topk"]
+    out["topk"]["executed_tflops"] = mult * out["topk"]["tflops"]
     # in-grid tokens per selected window (16 for an inner window, 4 or 1 at the edges)
     out["fine"]["selected_tokens_per_window"] = float(sel.double().sum()) / idx.numel()
     if fine_windows_ms is not None:
