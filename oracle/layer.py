@@ -373,8 +373,9 @@ def select_topk_probability(q, k_cmp, geom, top_k: int, block: int, blocks, firs
     ranked = np.empty((H, n, top_k + 1))
     for h in range(H):
         idx[h], r = _topk_rows(sc[h], top_k, first)
-        with np.errstate(divide="ignore"):
-            ranked[h] = np.log(r)
+        # a missing (K+1)-th entry stays -inf, as in select_topk
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ranked[h] = np.where(r > 0, np.log(np.maximum(r, 0.0)), -np.inf)
     return idx, ranked
 
 

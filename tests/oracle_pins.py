@@ -678,12 +678,15 @@ def pin_probability_equal_queries_is_logit_order():
         q[members] = q[members[0]]
     blocks = list(range(len(qbt)))
     q_blk = L.pooled_queries(q, G_SMALL, 4, blocks=blocks)
-    for K in (1, 3, 6):
+    for K in (1, 3, 6, kc.shape[0]):
         i_p, r_p = L.select_topk_probability(q, kc, G_SMALL, K, 4, blocks)
         i_l, r_l = L.select_topk(q_blk, kc, K)
         assert np.array_equal(i_p, i_l), K
-        diff = r_p - r_l
-        _close(diff, np.broadcast_to(diff[..., :1], diff.shape), 1e-12)
+        assert np.array_equal(np.isinf(r_p), np.isinf(r_l)), K   # K = all: no (K+1)-th, -inf
+        fin = np.isfinite(r_l)
+        diff = r_p[fin] - r_l[fin]                                 # one constant per (head, block)
+        first = np.broadcast_to((r_p[..., :1] - r_l[..., :1]), r_l.shape)[fin]
+        _close(diff, first, 1e-12)
 
 
 def pin_probability_key_shift_invariance():

@@ -77,7 +77,8 @@ MUTATIONS = [
      "s = (qq[qbt[bb], h, :] @ kh.T)"),
     ("prob_first_token_only", "probability_block_scores", "s = (qq[qbt[bb], h, :] @ kh.T) / math.sqrt(d)",
      "s = (qq[qbt[bb][:1], h, :] @ kh.T) / math.sqrt(d)"),
-    ("prob_ranked_not_log", "select_topk_probability", "ranked[h] = np.log(r)", "ranked[h] = r"),
+    ("prob_ranked_not_log", "select_topk_probability",
+     "ranked[h] = np.where(r > 0, np.log(np.maximum(r, 0.0)), -np.inf)", "ranked[h] = r"),
     ("diag_own_frame_masked", "_subsampled_token_diagonal", "s_c = (qc @ ckh.T) * scale + bias_c",
      "s_c = (qc @ ckh.T) * scale + bias_c; s_c[:, :m] = -np.inf"),
 ]
