@@ -328,6 +328,13 @@ def test_reference_frame_kept(geom, top_k):
         want = oracle.fine_attention(qh, kh, vh, geom, 4, ridx, keep_special=keep_special,
                                      keep_ref=True)
         assert_close(host(o_slc), want, geom.dtype, f"o_slc (reference frame, specials={keep_special})")
+        # the gate folded in, over the same index sets (o_cmp: any shared input)
+        o_cmp = torch.flip(q, dims=[0]).contiguous()
+        o_g = sga.gsa_sparse_attn_gated(q, k, v, idx_in, o_cmp, w, b, geom, top_k, keep_special=keep_special,
+                                        keep_ref=True)
+        _sync()
+        assert_close(host(o_g), oracle.gate(qh, host(o_cmp), want, host(w), host(b)), geom.dtype,
+                     f"gated fine (reference frame, specials={keep_special})")
     if top_k > 1:
         slipped = idx_in.clone()
         slipped[..., 0] = 0       # a window of frame 0: must add nothing
