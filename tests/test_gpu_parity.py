@@ -835,6 +835,9 @@ def test_scene1000_repeat(scene1000):
                                                  pooled_q=True),
         "gsa zero-padded": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True,
                                                  include_pad=True),
+        "gsa probability scores": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16, keep_intermediates=True,
+                                                        probability_scores=True),
+        "gsa fused gate": lambda: sga.gsa_layer(q, k, v, w, b, geom, 16),
     }
     for name, fn in calls.items():
         _announce(f"scene1000 repeat: {name}")
