@@ -84,9 +84,10 @@ __device__ __forceinline__ void loads_landed_barrier() {
   __syncthreads();
 }
 
-// planes[h][key] = (hi[64], lo[64]) of k_cmp[key, h, :]: a thread per 8 values.
+// planes[h][key] = (hi[64], lo[64]) of scale * k_cmp[key, h, :] (fp32 product,
+// then split): a thread per 8 values. scale 1 leaves the keys exact.
 __global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict__ k_cmp, long long n_keys,
-                                                        int n_heads, u32x4* __restrict__ planes) {
+                                                        int n_heads, float scale, u32x4* __restrict__ planes) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_keys * n_heads * 8) return;
   const int chunk = (int)(i & 7);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict
   const f32x4 a = *reinterpret_cast<const f32x4*>(src);
   const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  for (int e = 0; e < 4; ++e) { x[e] = a[e] * scale; x[4 + e] = b[e] * scale; }
   u32x4 hi, lo;
   split8(x, hi, lo);
   u32x4* dst = planes + ((long long)h * n_keys + key) * (kPlaneRowBytes / 16);
@@ -886,6 +887,8 @@ int resident_workgroups(const void* kernel, int threads, size_t lds) {
 // mean over a query block's tokens of their compressed-branch softmax
 // probabilities, Speed3R technical summary section 2.1), top_k <= 16.
 //
+// The key planes hold log2(e) k~ (fp32 product, then split), so the products
+// below are logits in log2 units.
 // 1. gsa_token_lse_kernel: every token's log-sum-exp over all pooled keys. The
 //    token's bf16 query times 1/8 is exact in bf16, so two bf16 products per
 //    operand chunk (q k_hi + q k_lo) give fp32-accurate logits; the layout is
@@ -923,7 +926,8 @@ __device__ __forceinline__ void load_row_eighth(const bf16* row, bool valid, int
 }
 
 // lse2[t, h] = log2 sum_j exp2(s_tj log2 e), s_tj = q_t . k~_j / 8, over all
-// n_total pooled keys; 128 tokens of one head per workgroup.
+// n_total pooled keys (planes of log2(e) k~); 128 tokens of one head per
+// workgroup.
 __global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf16* __restrict__ q,
                                                               const void* __restrict__ planes,
                                                               long long n_total, int n_rowtiles,
@@ -973,7 +977,7 @@ __global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf1
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i] * kLog2e;
+        float x = s[kb][i];
         if (!more) {  // the last tile: keys past the end take no part
           const long long j = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
           if (j >= n_total) x = -INFINITY;
@@ -1072,9 +1076,9 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf1
       }
       float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p0 += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nl[i]));
+      for (int i = 0; i < 8; ++i) p0 += __builtin_amdgcn_exp2f(acc[i] + nl[i]);
 #pragma unroll
-      for (int i = 8; i < 16; ++i) p1 += __builtin_amdgcn_exp2f(fmaf(acc[i], kLog2e, nl[i]));
+      for (int i = 8; i < 16; ++i) p1 += __builtin_amdgcn_exp2f(acc[i] + nl[i]);
       p0 += __shfl_xor(p0, 32);
       p1 += __shfl_xor(p1, 32);
       const int j = (int)u0 + kb * 32 + li;
@@ -1147,7 +1151,7 @@ hipError_t launch_gsa_topk_prob(const Geom& g, const void* q, const float* k_cmp
     const long long blocks = (n + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cmp, n_total,
-                       g.n_heads, static_cast<u32x4*>(planes));
+                       g.n_heads, kLog2e, static_cast<u32x4*>(planes));
     if (hipError_t e = hipGetLastError()) return e;
   }
   const bf16* qb = static_cast<const bf16*>(q);
@@ -1198,7 +1202,7 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
     const long long blocks = (n + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(split_keys_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cmp, n_total,
-                       g.n_heads, static_cast<u32x4*>(planes));
+                       g.n_heads, 1.f, static_cast<u32x4*>(planes));
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (top_k <= kRegK) {
