@@ -946,7 +946,12 @@ __global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf1
 
   PlaneTiles tiles;
   tiles.init(planes, n_total, h, 0, n_total, tid);
-  float m2 = -INFINITY, l = 0.f;  // running max (log2 units) and sum over this lane's keys
+  // m2: the lane's reference (log2 units), l: the sum of exp2(s - m2) over the
+  // lane's keys so far. The accumulators start at -m2, so the MFMA returns
+  // s - m2 and a term costs one exp2. The reference moves only on the first
+  // tile (to its maximum) and when a tile's terms sum past 2^32, where that
+  // tile is taken again against its own maximum.
+  float m2 = 0.f, l = 0.f;
   const long long n_tiles = (n_total + kTileN - 1) / kTileN;
   tiles.issue(0, smem, wave);
   for (long long it = 0; it < n_tiles; ++it) {
@@ -962,7 +967,7 @@ __global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf1
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = -m2;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 ah = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
@@ -972,34 +977,45 @@ __global__ __launch_bounds__(256, 4) void gsa_token_lse_kernel(Geom g, const bf1
       }
       s[kb] = acc;
     }
-    float mx = -INFINITY;
+    if (!more) {  // the last tile: keys past the end take no part
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[kb][i];
-        if (!more) {  // the last tile: keys past the end take no part
+        for (int i = 0; i < 16; ++i) {
           const long long j = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (j >= n_total) x = -INFINITY;
+          if (j >= n_total) s[kb][i] = -INFINITY;
         }
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    if (mx > m2) {
-      l *= __builtin_amdgcn_exp2f(m2 - mx);
-      m2 = mx;
     }
-    // (a lane whose keys so far all lie past the end keeps l = 0: -inf - -inf
-    // would be NaN)
-    const float base = m2 > -INFINITY ? m2 : 0.f;
+    float ts = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(s[kb][i] - base);
+      for (int i = 0; i < 16; ++i) ts += __builtin_amdgcn_exp2f(s[kb][i]);
+    if (it == 0 || !(ts <= 0x1p32f)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      // (a lane whose keys in this tile all lie past the end keeps its
+      // reference: -inf - -inf would be NaN)
+      const float sh = mx > -INFINITY ? mx : 0.f;
+      ts = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ts += __builtin_amdgcn_exp2f(s[kb][i] - sh);
+      // (on the first tile l is 0 and sh may lie far below the start value)
+      l = it == 0 ? 0.f : l * __builtin_amdgcn_exp2f(-sh);
+      m2 += sh;
+    }
+    l += ts;
   }
-  const float mo = __shfl_xor(m2, 32), lo = __shfl_xor(l, 32);
-  const float mm = fmaxf(m2, mo);
-  const float lt = l * __builtin_amdgcn_exp2f(m2 - mm) + lo * __builtin_amdgcn_exp2f(mo - mm);
+  // a lane with no key at all (only when every key fits one tile) holds l = 0
+  const float me = l > 0.f ? m2 : -INFINITY;
+  const float mo = __shfl_xor(me, 32), lo = __shfl_xor(l, 32);
+  const float mm = fmaxf(me, mo);
+  const float lt = l * __builtin_amdgcn_exp2f(me - mm) + lo * __builtin_amdgcn_exp2f(mo - mm);
   if (tvalid && hh == 0) lse2[t * g.n_heads + h] = mm + __log2f(lt);
 }
 
@@ -1064,9 +1080,11 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf1
     const unsigned char* lo_p = hi_p + kTileBytes;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      // the accumulator starts at -lse2 of its row, so the MFMA returns the
+      // log2 probability (-inf for an empty slot)
       f32x16 acc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = nl[i];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const u32x4 bh = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
@@ -1076,9 +1094,9 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf1
       }
       float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p0 += __builtin_amdgcn_exp2f(acc[i] + nl[i]);
+      for (int i = 0; i < 8; ++i) p0 += __builtin_amdgcn_exp2f(acc[i]);
 #pragma unroll
-      for (int i = 8; i < 16; ++i) p1 += __builtin_amdgcn_exp2f(acc[i] + nl[i]);
+      for (int i = 8; i < 16; ++i) p1 += __builtin_amdgcn_exp2f(acc[i]);
       p0 += __shfl_xor(p0, 32);
       p1 += __shfl_xor(p1, 32);
       const int j = (int)u0 + kb * 32 + li;

@@ -739,6 +739,46 @@ def test_probability_block_scores(geom):
             assert rel < 1e-4
 
 
+def test_probability_rising_logits():
+    """Logits that rise by hundreds of log2 units from frame to frame (the
+    first frame's far below zero): each token's log-sum-exp must move its
+    reference several times along the key stream and still match the oracle."""
+    geom = Geometry(6, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"probability-mean selection, rising logits {geom}")
+    q, k, v = make_qkv(geom, seed=43, device=DEV, distribution="scene")
+    gen = torch.Generator().manual_seed(44)
+    u = torch.randn(geom.n_heads, 64, generator=gen, dtype=torch.float64)
+    u = (u / u.norm(dim=1, keepdim=True)).to(torch.float32)
+    L = geom.n_special + geom.grid_h * geom.grid_w
+    s_f = torch.tensor([-60.0, -20.0, 0.0, 10.0, 20.0, 40.0]).repeat_interleave(L)
+    q = (q.float() + 30.0 * u.to(DEV)).to(torch.bfloat16).contiguous()
+    k = (k.float() + s_f.to(DEV)[:, None, None] * u.to(DEV)).to(torch.bfloat16).contiguous()
+    _, _, k32, _ = sga.gsa_compress(q, k, v, geom)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    rkc, _ = oracle.compress(kh, vh, geom, 4)
+    blocks = list(range(geom.n_frames * _nqb(geom)))
+    psc = oracle.probability_block_scores(qh, rkc, geom, 4, blocks)
+    idx, sc = sga.gsa_select_topk_probability(q, k32, geom, 16, want_score=True)
+    _sync()
+    ridx, ranked = oracle.select_topk_probability(qh, rkc, geom, 16, 4, blocks)
+    idx_h = host(idx).astype(np.int64)
+    check_topk(idx_h, ridx, ranked, None, None, "probability top-16, rising logits",
+               score_of=lambda h, bi, picks: np.log(psc[h, bi, picks]))
+    want = np.take_along_axis(psc, idx_h, axis=2)
+    rel = np.max(np.abs(host(sc) - want) / want)
+    # The kernels hold each key times log2(e) as two bf16 planes (hi + lo,
+    # 2^-18 relative), so a logit s carries an error up to 2^-18 A with
+    # A = sum_i |q_i k_i| log2(e) / 8, and s - lse up to twice that: the
+    # probability's relative error is bounded by ln(2) 2^-17 max A.
+    a_max = max(float((np.abs(qh[:, h]) @ np.abs(rkc[:, h]).T).max()) for h in range(geom.n_heads))
+    a_max *= math.log2(math.e) / 8
+    tol = 1e-4 + math.log(2) * 2.0 ** -17 * a_max
+    print(f"[parity] probability scores, rising logits: max rel err {rel:.2e} (bound {tol:.2e}, "
+          f"max A {a_max:.0f} log2 units)", flush=True)
+    assert rel < tol
+
+
 def test_gsa128_probability_scores():
     _gsa_check("gsa128", rows_cap=1024, probability_scores=True)
 
