@@ -290,3 +290,13 @@ def test_python_layer_requires_gpu_tensors():
     x = torch.zeros((16, 1, 64))
     with pytest.raises(ValueError, match="GPU tensor"):
         sga.dense_global_attn(x, x, x, gm)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises; nothing falls back to a
+    CPU path."""
+    import sparse_attention_global_amd._lib as lib_mod
+    monkeypatch.setattr(lib_mod, "_lib", None)
+    monkeypatch.setattr(lib_mod, "_LIB_PATH", str(tmp_path / "libsga.so"))
+    with pytest.raises(RuntimeError, match="is not built"):
+        lib_mod.library()
