@@ -162,6 +162,10 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
  * ws: sga_workspace_size(geom, SGA_OP_TOPK_PROB, top_k, keep, &bytes) bytes:
  *   the key planes of gsa_select_topk, then every token's log-sum-exp (fp32
  *   [T, H]).
+ * Accuracy: the keys enter as bf16 hi + lo planes, so each logit is within
+ *   2^-18 * sum_i |q_i k_i| / sqrt(d) of its exact value and a reported score
+ *   within a relative 2^-17 * max_(t,j) sum_i |q_i k_i| / sqrt(d) (plus fp32
+ *   rounding) of the exact mean probability.
  */
 sga_status gsa_select_topk_probability(const sga_geom* geom, int32_t block, const void* q,
                                        const float* k_cmp_f32, int32_t top_k, int32_t keep,
