@@ -315,18 +315,26 @@ struct FlashWaveState {
   // One staged 64-key tile, straight-line: both halves' scores, then for each
   // half its probabilities and O^T += V^T P^T. With MASKED, mask(kb, s) applies
   // the tile's key mask and logit bias (log2 units) to half kb's scores.
+  // Consecutive MFMAs share their B operand (the two key halves against one Q
+  // chunk; the two d halves against one P chunk): fewer operand bits toggle
+  // on a power-limited clock, and each accumulator chain keeps its order.
   template <bool MASKED, class MaskFn>
   __device__ __forceinline__ void tile(const unsigned char* stage, const TileLaneOffsets& off,
                                        const u32x4 qB[4], MaskFn&& mask) {
     f32x16 s[2];
+    {
+      u32x4 ka[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 ka[4];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) ka[ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
-      s[kb] = mfma32(ka[0], qB[0], negm);
+        for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
+      s[0] = mfma32(ka[0][0], qB[0], negm);
+      s[1] = mfma32(ka[1][0], qB[0], negm);
 #pragma unroll
-      for (int ks = 1; ks < 4; ++ks) s[kb] = mfma32(ka[ks], qB[ks], s[kb]);
+      for (int ks = 1; ks < 4; ++ks) {
+        s[0] = mfma32(ka[0][ks], qB[ks], s[0]);
+        s[1] = mfma32(ka[1][ks], qB[ks], s[1]);
+      }
     }
     if constexpr (MASKED) {
       mask(0, s[0]);
@@ -350,9 +358,9 @@ struct FlashWaveState {
         l = sum_bf16x8(pB[mm], l);
       }
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) oacc[db] = mfma32(va[2 * db + mm], pB[mm], oacc[db]);
+        for (int db = 0; db < 2; ++db) oacc[db] = mfma32(va[2 * db + mm], pB[mm], oacc[db]);
     }
   }
 
