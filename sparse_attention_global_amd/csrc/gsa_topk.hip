@@ -240,21 +240,23 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
     const unsigned char* hi_p = smem + stage * kStageBytes;
     const unsigned char* lo_p = hi_p + kTileBytes;
 
+    // both key halves against one query chunk back to back (a shared B
+    // operand); each score keeps its product order lo.hi, hi.lo, hi.hi
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc;
+    for (int i = 0; i < 16; ++i) { s[0][i] = 0.f; s[1][i] = 0.f; }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 ah = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
-        const u32x4 al = ld16(lo_p + t_off(kb * 32 + li, 2 * ks + hh));
-        acc = mfma32(al, qh[ks], acc);
-        acc = mfma32(ah, ql[ks], acc);
-        acc = mfma32(ah, qh[ks], acc);
-      }
-      s[kb] = acc;
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 ah0 = ld16(hi_p + t_off(li, 2 * ks + hh));
+      const u32x4 al0 = ld16(lo_p + t_off(li, 2 * ks + hh));
+      const u32x4 ah1 = ld16(hi_p + t_off(32 + li, 2 * ks + hh));
+      const u32x4 al1 = ld16(lo_p + t_off(32 + li, 2 * ks + hh));
+      s[0] = mfma32(al0, qh[ks], s[0]);
+      s[1] = mfma32(al1, qh[ks], s[1]);
+      s[0] = mfma32(ah0, ql[ks], s[0]);
+      s[1] = mfma32(ah1, ql[ks], s[1]);
+      s[0] = mfma32(ah0, qh[ks], s[0]);
+      s[1] = mfma32(ah1, qh[ks], s[1]);
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -403,21 +405,23 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
     const unsigned char* hi_p = smem + stage * kStageBytes;
     const unsigned char* lo_p = hi_p + kTileBytes;
 
+    // both key halves against one query chunk back to back (a shared B
+    // operand); each score keeps its product order lo.hi, hi.lo, hi.hi
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 acc;
+    for (int i = 0; i < 16; ++i) { s[0][i] = 0.f; s[1][i] = 0.f; }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 ah = ld16(hi_p + t_off(kb * 32 + li, 2 * ks + hh));
-        const u32x4 al = ld16(lo_p + t_off(kb * 32 + li, 2 * ks + hh));
-        acc = mfma32(al, qh[ks], acc);
-        acc = mfma32(ah, ql[ks], acc);
-        acc = mfma32(ah, qh[ks], acc);
-      }
-      s[kb] = acc;
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 ah0 = ld16(hi_p + t_off(li, 2 * ks + hh));
+      const u32x4 al0 = ld16(lo_p + t_off(li, 2 * ks + hh));
+      const u32x4 ah1 = ld16(hi_p + t_off(32 + li, 2 * ks + hh));
+      const u32x4 al1 = ld16(lo_p + t_off(32 + li, 2 * ks + hh));
+      s[0] = mfma32(al0, qh[ks], s[0]);
+      s[1] = mfma32(al1, qh[ks], s[1]);
+      s[0] = mfma32(ah0, ql[ks], s[0]);
+      s[1] = mfma32(ah1, ql[ks], s[1]);
+      s[0] = mfma32(ah0, qh[ks], s[0]);
+      s[1] = mfma32(ah1, qh[ks], s[1]);
     }
     if (!more) {  // the last tile: keys past the end score -inf
 #pragma unroll
