@@ -14,7 +14,10 @@ from typing import Optional
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsga.so")
+# The in-tree build; SGA_LIBRARY names another build of the same sources (the
+# host-sanitizer build the ABI tests load).
+_LIB_PATH = os.environ.get("SGA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libsga.so")
 _lib = None
 
 SGA_BF16, SGA_F32 = 0, 1

@@ -35,30 +35,33 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libsga.so)")
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [_hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj: str, extra=()) -> None:
+    cmd = [_hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every source and link libsga.so; returns the library path."""
-    out_dir = os.path.join(ROOT, "_build")
+def build(jobs: int = 8, verbose: bool = False, lib: str = LIB, obj_dir: str = "",
+          extra_flags=(), link_flags=()) -> str:
+    """Compile every source and link the library (default: the in-tree
+    libsga.so); returns its path. ``extra_flags`` go to every compile line,
+    ``link_flags`` to the link line."""
+    out_dir = obj_dir or os.path.join(ROOT, "_build")
     os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "capi.cpp")]
     objs = [os.path.join(out_dir, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        list(ex.map(_compile, srcs, objs))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        list(ex.map(lambda so: _compile(so[0], so[1], extra_flags), zip(srcs, objs)))
+    tmp = lib + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *link_flags, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
-    return LIB
+        print(f"built {lib}", file=sys.stderr)
+    return lib
 
 
 if __name__ == "__main__":

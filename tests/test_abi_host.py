@@ -300,3 +300,28 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(lib_mod, "_LIB_PATH", str(tmp_path / "libsga.so"))
     with pytest.raises(RuntimeError, match="is not built"):
         lib_mod.library()
+
+
+def test_workspace_size_sweep():
+    """Every workspace query over a sweep of geometries, from one token to
+    about 2^31 tokens: each returns OK or a validation status, never a size
+    that shrinks when the frame count grows (the host layout arithmetic is
+    checked for overflow by the sanitizer build of this file's tests)."""
+    cases = []
+    for n_frames in (1, 2, 7, 1000, 100_000, 1_000_000):
+        for (gh, gw, S) in ((1, 1, 0), (37, 37, 5), (9, 13, 16)):
+            for H in (1, 16):
+                for dt in (0, 1):
+                    cases.append(geom(n_frames=n_frames, grid_h=gh, grid_w=gw, n_special=S, n_heads=H,
+                                      dtype=dt))
+    ops = [(2, 0, 0), (2, 0, 1), (2, 100, 0), (1, 4, 4), (1, 1, 1), (1, 9, 9), (3, 1, 0), (3, 3, 0),
+           (4, 1, 0), (4, 16, 0), (4, 17, 0), (4, 128, 2), (5, 0, 0), (6, 16, 0), (6, 4, 2)]
+    last = {}
+    for g in cases:
+        for op in ops:
+            st, n = _ws(g, *op)
+            assert st in (OK, INVALID, UNSUPPORTED), (op, st)
+            if st == OK:
+                key = (g.grid_h, g.grid_w, g.n_special, g.n_heads, g.dtype, op)
+                assert n >= last.get(key, 0), (key, n)
+                last[key] = n
