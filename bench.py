@@ -16,7 +16,13 @@ compressed branch; pooling of the zero-padded grid), the AVGGT subsampling facto
 diagonal, and AVGGT's layer schedule (frame attention for the early layers,
 subsampled after) at 100, 300 and 800 frames.
 
-Prints one JSON line. `value` = tokens of the batch / seconds per step.
+Then the GSA form at 128 frames and the subsampled form at 256 frames are each
+timed against dense attention at the same size, and the fp64 CPU oracle is
+timed on a seeded row sample of every form of the step.
+
+Prints one JSON line. `value` = tokens of the batch / seconds per step. The
+per-form rates and speed-ups also appear as plain numbers in `roofline` and
+`cpu_baseline`, whose scalar fields the run record keeps.
 """
 from __future__ import annotations
 
@@ -41,8 +47,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="scene1000")
-    ap.add_argument("--cpu-rows", type=int, default=384,
-                    help="query rows of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="query rows of the CPU-oracle baseline's dense sample (0 disables the "
+                         "baseline); frame and subsampled attention take 8x, GSA 2x as many rows")
+    ap.add_argument("--cpu-rows-all", type=int, default=0,
+                    help="if set, every form's CPU sample takes this many rows (e.g. 4096)")
+    ap.add_argument("--small-configs", type=int, default=1,
+                    help="also time the 128-frame GSA and 256-frame subsampled configurations "
+                         "against dense at the same size (0 skips them)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--variant-steps", type=int, default=1,
                     help="timed passes of each GSA variant after one untimed pass (0 skips them)")
@@ -290,9 +302,36 @@ def main():
         roofline["traffic"] = traffic
         roofline["traffic_unit"] = "bytes per launch (HBM read + write, rocprofv3 FETCH_SIZE/WRITE_SIZE scaled)"
 
+    small = None
+    if args.small_configs:
+        del q, k, v
+        torch.cuda.empty_cache()
+        small = small_config_speedups(sga, torch, make_qkv, make_gate, args.seed, dev)
+        q, k, v = make_qkv(geom, seed=args.seed, device=dev, distribution=wl.distribution)
+
     cpu = None
     if args.cpu_rows > 0:
-        cpu = cpu_baseline(q, k, v, w, b, geom, wl, args.cpu_rows, args.seed)
+        rows_per_form = ({f: args.cpu_rows_all for f in ("dense", "frame", "gsa", "subsampled")}
+                         if args.cpu_rows_all else
+                         {"dense": args.cpu_rows, "frame": 8 * args.cpu_rows, "gsa": 2 * args.cpu_rows,
+                          "subsampled": 8 * args.cpu_rows})
+        cpu = cpu_baseline(q, k, v, w, b, geom, wl, rows_per_form, args.seed, layers)
+
+    # the per-form figures as plain numbers in the two objects whose scalar
+    # fields the run record keeps
+    roofline["dense_tokens_per_s"] = layers["dense"]["tokens_per_s"]
+    roofline["gsa_tokens_per_s"] = layers["gsa"]["tokens_per_s"]
+    roofline["subsampled_tokens_per_s"] = layers["subsampled"]["tokens_per_s"]
+    roofline["frame_tokens_per_s"] = layers["frame"]["tokens_per_s"]
+    roofline["gsa_speedup_vs_dense"] = layers["gsa"]["speedup_vs_dense"]
+    roofline["subsampled_speedup_vs_dense"] = layers["subsampled"]["speedup_vs_dense"]
+    roofline["gsa_compressed_mfma_frac"] = layers["gsa"]["compressed_mfma_frac"]
+    roofline["gsa_topk_ms"] = layers["gsa"]["kernels_ms"]["topk"]
+    roofline["subsampled_mfma_frac"] = layers["subsampled"]["mfma_frac"]
+    if small is not None:
+        roofline["gsa128_speedup_vs_dense"] = small["gsa128"]["speedup_vs_dense"]
+        roofline["sga256_speedup_vs_dense"] = small["sga256"]["speedup_vs_dense"]
+        layers["small_configs"] = small
 
     line = {
         "metric": METRIC, "value": T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -305,7 +344,11 @@ def main():
                                f"subsampled({sh}x{sw})",
                    "frames": N, "tokens": T, "heads": H, "head_dim": d, "top_k": wl.top_k,
                    "stride": [sh, sw]},
-        "layers": layers, "roofline": roofline, "cpu_baseline": cpu,
+        "layers": layers,
+        "forms": {n: {"tokens_per_s": layers[n]["tokens_per_s"], "ms": layers[n]["ms"],
+                      "speedup_vs_dense": per["dense"] / layers[n]["ms"]}
+                  for n in ("dense", "frame", "gsa", "subsampled")},
+        "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
@@ -420,44 +463,99 @@ def measured_traffic(workload):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(q, k, v, w, b, geom, wl, n_rows, seed):
-    """Time the fp64 oracle, as it stands, on a bounded sample of the same step."""
-    import numpy as np
+def cpu_baseline(q, k, v, w, b, geom, wl, rows_per_form, seed, layers):
+    """Time the fp64 oracle, as it stands, on a bounded sample of each form of
+    the step (a seeded row sample per form, all heads), on this host's cores."""
     import oracle
     from synth import sample_rows
 
     try:
-        cores = len(os.sched_getaffinity(0))
+        host_cores = len(os.sched_getaffinity(0))
     except AttributeError:
-        cores = os.cpu_count() or 1
-    workers = max(1, min(16, cores))
-    print(f"[bench] cpu baseline: copying inputs to host, {workers} oracle threads",
-          file=sys.stderr, flush=True)
+        host_cores = os.cpu_count() or 1
+    workers = max(1, min(16, host_cores))
+    print(f"[bench] cpu baseline: copying inputs to host; {host_cores} host cores, "
+          f"{workers} oracle threads", file=sys.stderr, flush=True)
     host = lambda x: x.detach().to("cpu").float().numpy()  # noqa: E731
     qh, kh, vh, wh, bh = host(q), host(k), host(v), host(w), host(b)
-    rows = sample_rows(geom.n_tokens, n_rows, seed=seed + 100).numpy()
     sh, sw = wl.stride
-    t0 = time.perf_counter()
-    oracle.dense_attention(qh, kh, vh, rows=rows, workers=workers)
-    t1 = time.perf_counter()
-    oracle.frame_attention(qh, kh, vh, geom, rows=rows)
-    t2 = time.perf_counter()
-    oracle.gsa_layer(qh, kh, vh, geom, wh, bh, wl.top_k, rows=rows, workers=workers)
-    t3 = time.perf_counter()
-    oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, rows=rows, workers=workers)
-    t4 = time.perf_counter()
-    total = t4 - t0
-    print(f"[bench] cpu baseline: dense {t1 - t0:.1f}s frame {t2 - t1:.1f}s gsa {t3 - t2:.1f}s "
-          f"subsampled {t4 - t3:.1f}s", file=sys.stderr, flush=True)
-    return {"value": len(rows) / total, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"{len(rows)} seeded query rows x all {geom.n_heads} heads through all four "
-                      f"forms (dense, frame, GSA incl. its full pooling, subsampled incl. its full "
-                      f"compaction), fp64 NumPy oracle; {total:.1f} s",
-            "seconds": {"dense": t1 - t0, "frame": t2 - t1, "gsa": t3 - t2,
-                        "subsampled": t4 - t3},
-            # the whole layer step at this rate (the pooling and compaction of the
-            # sample are whole-batch already, so this overstates them)
-            "extrapolated_full_step_s": total * geom.n_tokens / len(rows)}
+    T = geom.n_tokens
+    calls = {
+        "dense": lambda r: oracle.dense_attention(qh, kh, vh, rows=r, workers=workers),
+        "frame": lambda r: oracle.frame_attention(qh, kh, vh, geom, rows=r),
+        "gsa": lambda r: oracle.gsa_layer(qh, kh, vh, geom, wh, bh, wl.top_k, rows=r, workers=workers),
+        "subsampled": lambda r: oracle.subsampled_attention(qh, kh, vh, geom, sh, sw, rows=r, workers=workers),
+    }
+    out = {"value": None, "unit": "tokens/s", "cores": workers, "host_cores": host_cores,
+           "oracle_threads": workers, "kind": "oracle"}
+    total_rows, total_s = 0, 0.0
+    for i, (form, fn) in enumerate(calls.items()):
+        rows = sample_rows(T, rows_per_form[form], seed=seed + 100 + i).numpy()
+        t0 = time.perf_counter()
+        fn(rows)
+        dt = time.perf_counter() - t0
+        rate = len(rows) / dt
+        out[f"{form}_rows"] = len(rows)
+        out[f"{form}_s"] = dt
+        out[f"{form}_tokens_per_s"] = rate
+        out[f"{form}_extrapolated_full_layer_s"] = T / rate
+        out[f"{form}_gpu_over_cpu"] = layers[form]["tokens_per_s"] / rate
+        total_rows += len(rows)
+        total_s += dt
+        print(f"[bench] cpu baseline {form}: {len(rows)} rows in {dt:.1f} s ({rate:.1f} rows/s)",
+              file=sys.stderr, flush=True)
+    # the whole step (all four forms) at the sampled per-form rates
+    step_s = sum(T / out[f"{f}_tokens_per_s"] for f in calls)
+    out["value"] = T / step_s
+    out["extrapolated_full_step_s"] = step_s
+    out["sample"] = (", ".join(f"{f} {out[f + '_rows']}" for f in calls) +
+                     f" seeded query rows x all {geom.n_heads} heads (GSA incl. its whole pooling, "
+                     f"subsampled incl. its whole compaction), fp64 NumPy oracle, {workers} threads; "
+                     f"{total_s:.1f} s")
+    return out
+
+
+def small_config_speedups(sga, torch, make_qkv, make_gate, seed, dev):
+    """The GSA form at 128 frames and the subsampled form at 256 frames against
+    dense attention at the same size (one untimed call each, then the median of
+    three timed ones)."""
+    from synth import WORKLOADS
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[1]
+
+    out = {}
+    for name in ("gsa128", "sga256"):
+        wl = WORKLOADS[name]
+        g = wl.geom
+        q, k, v = make_qkv(g, seed=seed, device=dev, distribution=wl.distribution)
+        ws_d = torch.empty(sga.dense_workspace_bytes(g, sga.SGA_BF16), dtype=torch.uint8, device=dev)
+        t_d = timed(lambda: sga.dense_global_attn(q, k, v, g, ws=ws_d))
+        if name == "gsa128":
+            w, b = make_gate(g.n_heads, g.head_dim, seed=seed, device=dev)
+            t_x = timed(lambda: sga.gsa_layer(q, k, v, w, b, g, wl.top_k))
+        else:
+            sh, sw = wl.stride
+            ws_s = torch.empty(sga.workspace_bytes(g, sh, sw, sga.SGA_BF16), dtype=torch.uint8, device=dev)
+            t_x = timed(lambda: sga.subsampled_global_attn(q, k, v, g, sh, sw, ws=ws_s))
+        T = g.n_tokens
+        out[name] = {"frames": g.n_frames, "dense_ms": t_d, "form_ms": t_x,
+                     "dense_tokens_per_s": T / t_d * 1e3, "form_tokens_per_s": T / t_x * 1e3,
+                     "speedup_vs_dense": t_d / t_x}
+        print(f"[bench] {name}: dense {t_d:.1f} ms, {'GSA' if name == 'gsa128' else 'subsampled'} "
+              f"{t_x:.1f} ms ({t_d / t_x:.1f}x)", file=sys.stderr, flush=True)
+        del q, k, v
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

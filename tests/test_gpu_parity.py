@@ -378,6 +378,69 @@ def test_topk_wide_ties_fall_back():
         assert np.max(np.abs(host(score)[:, ::37] - ranked[:, :, :top_k])) < 1e-4
 
 
+@pytest.mark.parametrize("keep_ref", [False, True])
+def test_topk_register_ties(keep_ref):
+    """Exact ties on the register-list selection (top_k <= 16): (a) every
+    competing pooled key equal, so every score ties and the lowest competing
+    indices win; (b) every competing key present in three identical copies
+    500 apart (500 = 4 mod 8: consecutive copies sit in the two different
+    lane halves of a block), with the distinct keys' scores planted 1.25e-3
+    apart, so each copy group ties exactly and the lower copies win. With the
+    reference frame kept, frame 0's blocks score far above the rest and must
+    still not be picked."""
+    geom = Geometry(16, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"register top-K ties, keep_ref={keep_ref} {geom}")
+    N, H = geom.n_frames, geom.n_heads
+    nk, nq = N * _nb(geom), N * _nqb(geom)
+    first = _nb(geom) if keep_ref else 0
+    rng = np.random.default_rng(17)
+    q32 = rng.standard_normal((nq, H, 64))
+    n0 = 500
+    assert 3 * n0 <= nk - first and n0 % 8 == 4
+    # (b) planted classes: block b's query is the unit vector of coordinate cls_q
+    base_cls = np.arange(n0) % 64
+    base_mag = np.empty(n0)
+    for c in range(64):
+        members = np.nonzero(base_cls == c)[0]
+        base_mag[members] = 1.0 + 0.01 * rng.permutation(len(members))
+    k_b = np.zeros((nk, H, 64))
+    k_b[:first, :, :] = 50.0          # frame 0 (kept whole, must not compete)
+    rest = first + 3 * n0
+    k_b[rest:, :, :] = -50.0          # the leftover keys score far below
+    for copy in range(3):
+        for h in range(H):
+            k_b[first + copy * n0 + np.arange(n0), h, base_cls] = base_mag
+    cls_q = rng.integers(0, 64, size=(nq, H))
+    q_b = np.zeros((nq, H, 64))
+    for h in range(H):
+        q_b[np.arange(nq), h, cls_q[:, h]] = 1.0
+    # (a) all competing keys equal
+    k_a = np.tile(rng.standard_normal((1, H, 64)), (nk, 1, 1))
+    if keep_ref:
+        k_a[:first] += 3.0
+    for top_k in (1, 4, 16):
+        idx_a = sga.gsa_select_topk(torch.tensor(q32, dtype=torch.float32, device=DEV),
+                                    torch.tensor(k_a, dtype=torch.float32, device=DEV), geom, top_k,
+                                    keep_ref=keep_ref)
+        idx_b, sc_b = sga.gsa_select_topk(torch.tensor(q_b, dtype=torch.float32, device=DEV),
+                                          torch.tensor(k_b, dtype=torch.float32, device=DEV), geom, top_k,
+                                          want_score=True, keep_ref=keep_ref)
+        _sync()
+        got_a = host(idx_a).astype(np.int64)
+        assert (got_a == first + np.arange(top_k)[None, None, :]).all(), ("all equal", top_k)
+        got_b = host(idx_b).astype(np.int64)
+        for h in range(H):
+            for bb in range(nq):
+                members = np.nonzero(base_cls == cls_q[bb, h])[0]
+                order = members[np.argsort(-base_mag[members], kind="stable")]
+                seq = [first + copy * n0 + i for i in order for copy in range(3)]
+                want = np.sort(seq[:top_k])
+                assert np.array_equal(got_b[h, bb], want), ("copies", top_k, h, bb, got_b[h, bb], want)
+        want_sc = np.take_along_axis(np.einsum("bhd,jhd->hbj", q_b, k_b), got_b, axis=2) / 8.0
+        assert np.max(np.abs(host(sc_b) - want_sc)) < 1e-5
+        print(f"[parity] register top-{top_k} ties (keep_ref={keep_ref}): all rows exact", flush=True)
+
+
 def test_topk_wide_few_candidates():
     """Fewer competing blocks than the bound's 128 buckets: the bound is -inf,
     every candidate is kept and sorted (3 frames x 12 blocks, top-20; 2 frames
@@ -599,6 +662,20 @@ def _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, top_k, name, keep_
     assert_close(host(o_fused)[rows], ref["o"], "bf16", f"{name} gate fused into fine (oracle sets, all rows)")
 
 
+def _layer_on_own_selection(qh, kh, vh, geom, w, b, out, o_layer, ref, rows, name, keep_ref, W):
+    """The GSA layer with the GPU's own top-K on every sampled row: the oracle's
+    fine branch and gate run on the index sets the GPU selected (each of them
+    already checked valid: exact on decided blocks, within the score gap
+    elsewhere), with the oracle's compressed branch; the GPU's fine branch,
+    its separate gate and the layer with the gate folded in must all match."""
+    idx_gpu = host(out["idx"]).astype(np.int32)
+    o_slc = oracle.fine_attention(qh, kh, vh, geom, 4, idx_gpu, rows=rows, keep_ref=keep_ref, workers=W)
+    o = oracle.gate(qh[rows], ref["o_cmp"], o_slc, host(w), host(b))
+    assert_close(host(out["o_slc"])[rows], o_slc, "bf16", f"{name} o_slc (own selection, all rows)")
+    assert_close(host(out["o"])[rows], o, "bf16", f"{name} gsa layer (own selection, all rows)")
+    assert_close(host(o_layer)[rows], o, "bf16", f"{name} gsa layer, fused gate (own selection, all rows)")
+
+
 def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=False,
                probability_scores=False):
     wl, geom, q, k, v = _workload_inputs(name)
@@ -641,13 +718,12 @@ def _gsa_check(name, rows_cap=None, keep_ref=False, pooled_q=False, include_pad=
     if keep.any():  # (with close block scores no sampled row may be decided in all 16 heads)
         assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", f"{name} o_slc")
         assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer")
-        # the layer as one returns it (the gate folded into the fine branch)
-        o_fused = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_ref=keep_ref, pooled_q=pooled_q,
-                                include_pad=include_pad, probability_scores=probability_scores)
-        _sync()
-        assert_close(host(o_fused)[rows][keep], ref["o"][keep], "bf16", f"{name} gsa layer (fused gate)")
-    else:
-        assert include_pad, "only the zero-padded pooling leaves no sampled row decided here"
+    # the layer as one calls it (the gate folded into the fine branch), on every
+    # sampled row
+    o_fused = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k, keep_ref=keep_ref, pooled_q=pooled_q,
+                            include_pad=include_pad, probability_scores=probability_scores)
+    _sync()
+    _layer_on_own_selection(qh, kh, vh, geom, w, b, out, o_fused, ref, rows, name, keep_ref, W)
     _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, name, keep_ref)
 
 
@@ -806,14 +882,18 @@ def scene1000():
 @pytest.mark.timeout(1200)
 def test_scene1000_dense(scene1000):
     wl, geom, q, k, v, probes, (qh, kh, vh) = scene1000
-    # 448 sampled rows + the 64 planted probes: every head, all d (the dense
-    # oracle over 1.374M keys costs ~2e9 fp64 flop per row)
-    rows = np.union1d(sample_rows(geom.n_tokens, 448, seed=5).numpy(), probes)
+    # 4096 sampled rows + the 64 planted probes: every head, all d (the dense
+    # oracle over 1.374M keys costs ~2e9 fp64 flop per row; eight passes, each
+    # reported)
+    rows = np.union1d(sample_rows(geom.n_tokens, wl.check_rows, seed=5).numpy(), probes)
     _announce(f"scene1000 dense, {len(rows)} rows")
     o = sga.dense_global_attn(q, k, v, geom)
     _sync()
-    ref = oracle.dense_attention(qh, kh, vh, rows=rows, workers=oracle_workers())
-    assert_close(host(o)[rows], ref, "bf16", "scene1000 dense")
+    ref = []
+    for part in np.array_split(rows, 8):
+        ref.append(oracle.dense_attention(qh, kh, vh, rows=part, workers=oracle_workers()))
+        print(f"[oracle] scene1000 dense: {sum(len(r) for r in ref)} rows", flush=True)
+    assert_close(host(o)[rows], np.concatenate(ref), "bf16", "scene1000 dense")
     assert_close(host(o)[probes], oracle.dense_attention(qh, kh, vh, rows=probes,
                                                          workers=oracle_workers()),
                  "bf16", "scene1000 dense planted probes")
@@ -853,6 +933,10 @@ def test_scene1000_gsa(scene1000):
     assert keep.sum() > 0
     assert_close(host(out["o_slc"])[rows][keep], ref["o_slc"][keep], "bf16", "scene1000 o_slc")
     assert_close(host(out["o"])[rows][keep], ref["o"][keep], "bf16", "scene1000 gsa layer")
+    o_fused = sga.gsa_layer(q, k, v, w, b, geom, wl.top_k)
+    _sync()
+    _layer_on_own_selection(qh, kh, vh, geom, w, b, out, o_fused, ref, rows, "scene1000", False, W)
+    del o_fused
     _fine_on_oracle_sets(q, k, v, geom, w, b, out, ref, rows, wl.top_k, "scene1000")
 
 
@@ -913,11 +997,12 @@ def test_scene1000_subsampled(scene1000):
 
 @pytest.mark.timeout(1200)
 def test_scene1000_variants(scene1000):
-    """The variants the benchmark times at 1000 frames, on 512 sampled rows:
-    top-128 selection, the VGGT reference frame (selection and fine branch),
-    the block-level compressed branch and the token-level AVGGT diagonal."""
+    """The variants the benchmark times at 1000 frames, on 4096 sampled rows:
+    top-128 selection, the VGGT reference frame (selection and fine branch, on
+    the oracle's index sets and on the GPU's own), the block-level compressed
+    branch and the token-level AVGGT diagonal."""
     wl, geom, q, k, v, probes, (qh, kh, vh) = scene1000
-    rows = sample_rows(geom.n_tokens, 512, seed=9).numpy()
+    rows = sample_rows(geom.n_tokens, wl.check_rows, seed=9).numpy()
     nb = _nb(geom)
     W = oracle_workers()
     _announce(f"scene1000 variants, {len(rows)} rows")
@@ -946,6 +1031,14 @@ def test_scene1000_variants(scene1000):
     assert_close(host(o_slc)[rows], oracle.fine_attention(qh, kh, vh, geom, 4, idx_full, rows=rows,
                                                           keep_ref=True, workers=W),
                  "bf16", "scene1000 o_slc (reference frame kept)")
+    # ... and on the GPU's own selection (checked valid above)
+    o_slc_own = sga.gsa_sparse_attn(q, k, v, idx_ref, geom, wl.top_k, keep_ref=True)
+    _sync()
+    assert_close(host(o_slc_own)[rows],
+                 oracle.fine_attention(qh, kh, vh, geom, 4, host(idx_ref).astype(np.int32), rows=rows,
+                                       keep_ref=True, workers=W),
+                 "bf16", "scene1000 o_slc (reference frame kept, own selection)")
+    del o_slc_own
     assert_close(host(o_blk)[rows], oracle.compressed_attention_pooled(qh, rkc, rvc, geom, 4,
                                                                       rows=rows, workers=W),
                  "bf16", "scene1000 o_cmp (block level)")
