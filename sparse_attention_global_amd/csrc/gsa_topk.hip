@@ -38,6 +38,10 @@ constexpr int kStageBytes = 2 * kTileBytes;   // hi + lo planes
 
 __device__ __forceinline__ int t_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
+// Whether any lane of the wave holds p (a lane mask from one compare; HIP's
+// __any materialises the predicate and compares it again).
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 __device__ __forceinline__ bool beats(float s, int j, float ts, int tj) {
   return s > ts || (s == ts && j < tj);
 }
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
         mx = fmaxf(mx, s[kb][i]);
       }
     // candidates can only beat the threshold if their score reaches it
-    if (__any(rvalid && mx >= tau_s)) {
+    if (wave_any(rvalid && mx >= tau_s)) {
       for (int half = 0; half < 2; ++half) {
         if (hh == half && rvalid && mx >= tau_s) {
 #pragma unroll
@@ -335,6 +339,11 @@ __global__ __launch_bounds__(256) void gsa_topk_kernel(Geom g, const float* __re
 // log2(kRegK) half-cleaner stages.
 // ---------------------------------------------------------------------------
 constexpr int kRegK = 16;
+// Tiles between refreshes of the block-wide 16th best (top_k == 16).
+#ifndef SGA_TOPK_UNION_EVERY
+#define SGA_TOPK_UNION_EVERY 8
+#endif
+constexpr int kUnionEvery = SGA_TOPK_UNION_EVERY;
 
 // Entry order: larger score first; equal scores, lower index first.
 __device__ __forceinline__ bool better(float s, int j, float ts, int tj) {
@@ -343,16 +352,37 @@ __device__ __forceinline__ bool better(float s, int j, float ts, int tj) {
 
 // Occupancy: 4 workgroups (4 waves per SIMD, 128 VGPRs); measured at 128 frames
 // 2.46 ms against 2.76 ms at 3 waves per SIMD and 3.40 ms at 2.
+// Listed rows (the blocks the two-stage selection could not certify): per
+// head the first count[h] entries of rows[h][.] ([H][n_rows] int32). The list
+// positions below `cap` (a multiple of 128) are split over n_seg key segments:
+// workgroup (h, tile, seg) streams segment seg of the keys for list entries
+// 128 tile .. 128 tile + 127 and stores each lane's list (exact scores, key
+// indices) to seg_val / seg_idx [H][cap][n_seg][32], for the merge kernel.
+// Positions from `cap` on stream all keys in segment 0's workgroup and write
+// their result directly.
+struct RegList {
+  const int32_t* rows;
+  const int32_t* count;
+  int n_seg;
+  int cap;
+  float* seg_val;
+  int32_t* seg_idx;
+};
+
+// list.rows == nullptr: workgroup w of head h selects rows 128 w .. 128 w + 127.
 template <bool FULL>  // FULL: top_k == kRegK, the threshold is the list's last slot
 __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const float* __restrict__ q_blk,
                                                            const void* __restrict__ planes,
                                                            long long n_total, long long n_cand, int j0,
                                                            int top_k, int n_rowtiles,
                                                            int32_t* __restrict__ idx,
-                                                           float* __restrict__ score) {
+                                                           float* __restrict__ score, RegList list) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int h = blockIdx.x / n_rowtiles;
-  const long long row0 = (long long)(blockIdx.x % n_rowtiles) * 128;
+  const int segs = list.rows != nullptr ? list.n_seg : 1;
+  const int seg = blockIdx.x % segs;
+  const int wg = blockIdx.x / segs;
+  const int h = wg / n_rowtiles;
+  const long long row0 = (long long)(wg % n_rowtiles) * 128;
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const long long rs = (long long)g.n_heads * kHeadDim;
   const long long hoff = (long long)h * kHeadDim;
@@ -360,8 +390,25 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, li = lane & 31;
-  const long long row = row0 + wave * 32 + li;
-  const bool rvalid = row < n_rows;
+  const long long pos = row0 + wave * 32 + li;  // the row, or the list position
+  long long row = pos;
+  bool rvalid = row < n_rows;
+  bool split = false;
+  const long long n_tiles_all = (n_cand + kTileN - 1) / kTileN;
+  long long it0 = 0, it1 = n_tiles_all;
+  if (list.rows != nullptr) {  // (uniform over the workgroup: it returns before any barrier)
+    const long long cnt = list.count[h];
+    if (row0 >= cnt) return;
+    split = row0 < list.cap;
+    if (!split && seg != 0) return;
+    rvalid = pos < cnt;
+    row = rvalid ? (long long)list.rows[(long long)h * n_rows + pos] : 0;
+    if (split) {
+      const long long per = (n_tiles_all + segs - 1) / segs;
+      it0 = min(n_tiles_all, seg * per);
+      it1 = min(n_tiles_all, it0 + per);
+    }
+  }
 
   // pooled-query operand scaled by 1/sqrt(64) = 1/8 (exact), hi and lo planes
   u32x4 qh[4], ql[4];
@@ -388,16 +435,16 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   int lj[kRegK];
 #pragma unroll
   for (int p = 0; p < kRegK; ++p) { lv[p] = -INFINITY; lj[p] = 0x7fffffff; }
-  float tau = -INFINITY;  // lv[top_k - 1]
+  float tau = -INFINITY;   // lv[top_k - 1]
+  float tblk = -INFINITY;  // the 16th best of the block's two lists (top_k == 16)
   const int kth = top_k - 1;
 
-  const long long n_tiles = (n_cand + kTileN - 1) / kTileN;
-  tiles.issue(0, smem, wave);
+  if (it0 < it1) tiles.issue(it0 * kTileN, smem, wave);
 
-  for (long long it = 0; it < n_tiles; ++it) {
-    const int stage = (int)(it & 1);
+  for (long long it = it0; it < it1; ++it) {
+    const int stage = (int)((it - it0) & 1);
     const long long u0 = it * kTileN;
-    const bool more = it + 1 < n_tiles;
+    const bool more = it + 1 < it1;
     // tile it has landed in every wave's loads, and every wave is done with
     // the other stage
     loads_landed_barrier();
@@ -437,14 +484,25 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    if (__any(rvalid && mx > tau)) {
+    // A block-wide bound on this lane's candidates: the partner lane holds
+    // top_k keys of the block scoring at least its threshold, and (with 16
+    // slots, refreshed every kUnionEvery tiles) the union of the two lists
+    // holds 16 keys scoring at least its 16th best. A key scoring below either
+    // cannot reach the block's final set; a key tying it still may (a lower
+    // index wins), so it is kept.
+    float tp;
+    {
+      const auto tsw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tau), __float_as_uint(tau), false, false);
+      tp = fmaxf(tblk, __uint_as_float(hh ? tsw[0] : tsw[1]));
+    }
+    if (wave_any(rvalid && mx > tau && mx >= tp)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float sv = s[kb][i];
-          const bool c = rvalid && sv > tau;
-          if (__any(c)) {
+          const bool c = rvalid && sv > tau && sv >= tp;
+          if (wave_any(c)) {
             const int j = (int)u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
             // Slot p of the new list is the median of (old p - 1, sv, old p):
             // the list is sorted, so that is old p - 1 when sv goes before it,
@@ -472,6 +530,30 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
           }
         }
     }
+    if (FULL && (it % kUnionEvery) == kUnionEvery - 1) {
+      // the union's 16th best: the best 16 of two lists sorted best first are
+      // max(a[p], b[15 - p]) (as in the final merge), so their minimum
+      float u = INFINITY;
+#pragma unroll
+      for (int p = 0; p < kRegK; ++p) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lv[kRegK - 1 - p]),
+                                                        __float_as_uint(lv[kRegK - 1 - p]), false, false);
+        u = fminf(u, fmaxf(lv[p], __uint_as_float(hh ? r[0] : r[1])));
+      }
+      tblk = u;
+    }
+  }
+
+  if (split) {  // this segment's lists, for the merge kernel
+    if (rvalid) {
+      const long long base = (((long long)h * list.cap + pos) * segs + seg) * 32 + hh * 16;
+#pragma unroll
+      for (int p = 0; p < kRegK; ++p) {
+        list.seg_val[base + p] = lv[p];
+        list.seg_idx[base + p] = lj[p] == 0x7fffffff ? 0x7fffffff : lj[p] + j0;
+      }
+    }
+    return;
   }
 
   // ---- merge the block's two lists (lanes l and l + 32) ------------------------
@@ -526,6 +608,366 @@ __global__ __launch_bounds__(256, 4) void gsa_topk_reg_kernel(Geom g, const floa
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Two-stage selection for top_k <= 16 (the default path while a lane's key
+// positions fit 16 bits, i.e. at most 2048 key tiles).
+//
+// Stage 1 (gsa_topk_approx_kernel) ranks by a single bf16 product per score,
+// s1 = bf16(q/8) . bf16(k), one third of the exact path's matrix-core work. A
+// list entry is one 32-bit word: the score's 16-bit order-preserving bucket
+// (sign, exponent, 7 mantissa bits) above a 16-bit inverted lane position, so
+// a larger word is a higher bucket or, within a bucket, an earlier key, and the
+// insertion network is one v_med3_u32 per slot. Each lane keeps its 16 best
+// words; a key enters iff its bucket is above the 16th word's bucket, i.e.
+// iff s1 reaches that bucket's upper edge U. Every key a lane drops therefore
+// has s1 < U of the lane's final 16th word.
+//
+// Stage 2 (gsa_topk_rescore_kernel) scores the block's 32 candidates exactly
+// (fp32, the same arithmetic for every candidate), sorts them (larger score
+// first, ties to the lower index) and certifies the result: with
+//   |s1 - s| <= (2^-7 + 2^-16 + 2^-17) sum_i |q_i k_i| <= 2^-6.9 |q| max|k|
+// (bf16 rounding of both operands, 64 fp32 additions) as the bound E, a
+// dropped key scores below max(U_A, U_B) + E, so when the K-th best candidate
+// scores strictly above that, the candidates' top-K is the block's top-K.
+// Blocks that miss the certificate (about 1% at 1000 frames, top-16) are
+// listed per head and selected again by the exact register kernel.
+// ---------------------------------------------------------------------------
+constexpr int kApproxMaxTiles = 2048;  // lane positions (32 per tile) fit 16 bits
+constexpr int kKnormChunks = 256;      // partial maxima of |k|^2 per head
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_order_key(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+// The smallest score whose bucket lies above the bucket of list word w (w != 0).
+__device__ __forceinline__ float bucket_upper(uint32_t w) {
+  const uint32_t b = w >> 16;
+  return b >= 0xff7fu ? INFINITY : from_order_key((b + 1u) << 16);
+}
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
+// Per (head, chunk) maximum of |k|^2 over the fp32 pooled keys; workgroup 0
+// also clears the per-head counts of the blocks stage 2 cannot certify.
+__global__ __launch_bounds__(256) void kmax_partial_kernel(const float* __restrict__ k_cmp, long long n_keys,
+                                                           int n_heads, float* __restrict__ out,
+                                                           int32_t* __restrict__ fail_count) {
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_heads) fail_count[threadIdx.x] = 0;
+  const int h = blockIdx.x / kKnormChunks, chunk = blockIdx.x % kKnormChunks;
+  const long long per = (n_keys + kKnormChunks - 1) / kKnormChunks;
+  const long long r0 = chunk * per, r1 = min(r0 + per, n_keys);
+  const int t = threadIdx.x, part = t & 7;
+  float best = 0.f;
+  for (long long r = r0 + (t >> 3); r < r1; r += 32) {
+    const float* kp = k_cmp + (r * n_heads + h) * kHeadDim + part * 8;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(kp);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(kp + 4);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(a[e], a[e], fmaf(b[e], b[e], acc));
+#pragma unroll
+    for (int sh = 1; sh < 8; sh <<= 1) acc += __shfl_xor(acc, sh);
+    best = fmaxf(best, acc);
+  }
+#pragma unroll
+  for (int sh = 8; sh < 64; sh <<= 1) best = fmaxf(best, __shfl_xor(best, sh));
+  __shared__ float wmax[4];
+  if ((t & 63) == 0) wmax[t >> 6] = best;
+  __syncthreads();
+  if (t == 0) out[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+// Stage 1: a workgroup owns 128 query blocks of one head (32 per wave) and
+// streams the hi plane of the competing keys through LDS, double buffered;
+// cand[h][row][32] receives lane hh = 0's 16 words then lane hh = 1's, each
+// lane's list best first.
+__global__ __launch_bounds__(256, 4) void gsa_topk_approx_kernel(Geom g, const float* __restrict__ q_blk,
+                                                              const void* __restrict__ planes,
+                                                              long long n_total, long long n_cand, int j0,
+                                                              int n_rowtiles, uint32_t* __restrict__ cand) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int h = blockIdx.x / n_rowtiles;
+  const long long row0 = (long long)(blockIdx.x % n_rowtiles) * 128;
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const long long rs = (long long)g.n_heads * kHeadDim;
+  const long long hoff = (long long)h * kHeadDim;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  const long long row = row0 + wave * 32 + li;
+  const bool rvalid = row < n_rows;
+
+  // pooled-query operand: bf16(q / 8) (the scale is exact)
+  u32x4 qh[4];
+  {
+    const float* qp = q_blk + (rvalid ? row : 0) * rs + hoff + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(qp + ks * 16);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(qp + ks * 16 + 4);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        qh[ks][e] = rvalid ? pack_bf16x2(a[2 * e] * 0.125f, a[2 * e + 1] * 0.125f) : 0u;
+        qh[ks][2 + e] = rvalid ? pack_bf16x2(b[2 * e] * 0.125f, b[2 * e + 1] * 0.125f) : 0u;
+      }
+    }
+  }
+
+  // hi plane of a 64-key tile: key row r (128 B) at r * 128 in the stage,
+  // logical chunk c at physical chunk c ^ (r & 7); two 16-byte loads per thread
+  const unsigned char* head = static_cast<const unsigned char*>(planes) +
+                              ((long long)h * n_total + j0) * kPlaneRowBytes;
+  uint32_t voff[2];
+#pragma unroll
+  for (int qd = 0; qd < 2; ++qd) {
+    const int o = qd * 4096 + tid * 16;
+    const int r = o >> 7, pc = (o >> 4) & 7;
+    voff[qd] = (uint32_t)(r * kPlaneRowBytes + ((pc ^ (r & 7)) << 4));
+  }
+  auto issue = [&](long long u0, unsigned char* stage) {
+    const long long rows = min((long long)kTileN, n_cand - u0);
+    const auto rsrc = buffer_rsrc(head + u0 * kPlaneRowBytes, rows * kPlaneRowBytes);
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) lds_dma16(rsrc, voff[qd], stage + qd * 4096 + wave * 1024);
+  };
+
+  uint32_t lv[kRegK];
+#pragma unroll
+  for (int p = 0; p < kRegK; ++p) lv[p] = 0u;  // 0: empty (no real score maps to word 0)
+  // a key enters iff s1 >= ut: any finite key while the list is not full; no
+  // key of a row past the end
+  constexpr float kAnyFinite = -3.4028234663852886e38f;
+  float ut = rvalid ? kAnyFinite : INFINITY;
+
+  const int n_tiles = (int)((n_cand + kTileN - 1) / kTileN);
+  issue(0, smem);
+  for (int it = 0; it < n_tiles; ++it) {
+    const int stage = it & 1;
+    const long long u0 = (long long)it * kTileN;
+    const bool more = it + 1 < n_tiles;
+    loads_landed_barrier();
+    if (more) issue(u0 + kTileN, smem + (stage ^ 1) * kTileBytes);
+    const unsigned char* hi_p = smem + stage * kTileBytes;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { s[0][i] = 0.f; s[1][i] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 a0 = ld16(hi_p + t_off(li, 2 * ks + hh));
+      const u32x4 a1 = ld16(hi_p + t_off(32 + li, 2 * ks + hh));
+      s[0] = mfma32(a0, qh[ks], s[0]);
+      s[1] = mfma32(a1, qh[ks], s[1]);
+    }
+    if (!more) {  // the last tile: keys past the end score -inf (never enter)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const long long j = u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (j >= n_cand) s[kb][i] = -INFINITY;
+        }
+    }
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    if (wave_any(mx >= ut)) {
+      // ut is refreshed once per tile: a stale (lower) threshold only lets more
+      // keys through the network, which keeps the best 16 words either way
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float sv = s[kb][i];
+          const bool c = sv >= ut;
+          if (wave_any(c)) {
+            // the new word, or 0 (below every slot: the list stays) where the
+            // lane does not take this key; slot p becomes the median of
+            // (old p - 1, new, old p), walking from the tail
+            const uint32_t pos = (uint32_t)(it * 32 + kb * 16 + i);
+            const uint32_t x = c ? ((order_key(sv) & 0xffff0000u) | (0xffffu - pos)) : 0u;
+#pragma unroll
+            for (int p = kRegK - 1; p >= 1; --p) lv[p] = med3u(lv[p - 1], x, lv[p]);
+            lv[0] = max(lv[0], x);
+          }
+        }
+      if (rvalid) ut = lv[kRegK - 1] ? bucket_upper(lv[kRegK - 1]) : kAnyFinite;
+    }
+  }
+  if (rvalid) {
+    u32x4* dst = reinterpret_cast<u32x4*>(cand + ((long long)h * n_rows + row) * 32 + hh * 16);
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) dst[c4] = u32x4{lv[4 * c4], lv[4 * c4 + 1], lv[4 * c4 + 2], lv[4 * c4 + 3]};
+  }
+}
+
+// Stage 2: 32 lanes per (head, query block), lane c holding candidate c of
+// the block's two lists. Exact fp32 scores, a bitonic sort across the 32
+// lanes, the certificate, then the block's top_k (ascending indices) or its
+// entry in the head's list of blocks for the exact kernel.
+__global__ __launch_bounds__(256) void gsa_topk_rescore_kernel(Geom g, const float* __restrict__ q_blk,
+                                                               const float* __restrict__ k_cmp, int j0,
+                                                               int top_k, const uint32_t* __restrict__ cand,
+                                                               const float* __restrict__ kmax_part,
+                                                               int32_t* __restrict__ idx, float* __restrict__ score,
+                                                               int32_t* __restrict__ fail_count,
+                                                               int32_t* __restrict__ fail_rows) {
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const long long pair = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+  const int c = threadIdx.x & 31;
+  const int lane = threadIdx.x & 63;
+  const bool pvalid = pair < n_rows * g.n_heads;
+  const long long pr = pvalid ? pair : 0;
+  const int h = (int)(pr / n_rows);
+  const long long row = pr % n_rows;
+  const long long rs = (long long)g.n_heads * kHeadDim;
+
+  // max |k| of the head (partials of |k|^2, rounded up for their own fp32 error)
+  float k2 = 0.f;
+  for (int i = c; i < kKnormChunks; i += 32) k2 = fmaxf(k2, kmax_part[h * kKnormChunks + i]);
+#pragma unroll
+  for (int sh = 1; sh < 32; sh <<= 1) k2 = fmaxf(k2, __shfl_xor(k2, sh));
+  const float kmax = sqrtf(k2 * 1.0001f);
+
+  const uint32_t w = cand[pr * 32 + c];
+  const uint32_t wa = __shfl(w, (lane & 32) + 15);   // lane hh = 0's 16th word
+  const uint32_t wb = __shfl(w, (lane & 32) + 31);   // lane hh = 1's
+  // candidate c's key: list c / 16, lane position p = 0xffff - (low 16 bits)
+  long long j = 0x7fffffffffffLL;
+  float sc = -INFINITY;
+  const float* qp = q_blk + row * rs + (long long)h * kHeadDim;
+  float q2 = 0.f;
+  if (w != 0u) {
+    const int p = 0xffff - (int)(w & 0xffffu);
+    const int hh = c >> 4;
+    const long long jl = (long long)(p >> 5) * kTileN + ((p >> 4) & 1) * 32 + 8 * ((p >> 2) & 3) + 4 * hh + (p & 3);
+    j = jl + j0;
+    const float* kp = k_cmp + (j * g.n_heads + h) * kHeadDim;
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < kHeadDim; e += 4) {
+      const f32x4 qa = *reinterpret_cast<const f32x4*>(qp + e);
+      const f32x4 ka = *reinterpret_cast<const f32x4*>(kp + e);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc = fmaf(qa[r] * 0.125f, ka[r], acc);
+    }
+    sc = acc;
+  }
+#pragma unroll
+  for (int e = 0; e < kHeadDim; e += 4) {
+    const f32x4 qa = *reinterpret_cast<const f32x4*>(qp + e);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) q2 = fmaf(qa[r] * 0.125f, qa[r] * 0.125f, q2);
+  }
+  // bitonic sort across the 32 lanes: larger score first, ties to the lower key
+  int jj = (int)min(j, 0x7fffffffLL);
+#pragma unroll
+  for (int size = 2; size <= 32; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride >= 1; stride >>= 1) {
+      const float os = __shfl_xor(sc, stride);
+      const int oj = __shfl_xor(jj, stride);
+      const bool other_better = os > sc || (os == sc && oj < jj);
+      const bool lower = (c & stride) == 0;          // this lane keeps the better of the pair ...
+      const bool desc = (c & size) == 0 || size == 32;  // ... in a descending run
+      const bool take = (lower == desc) ? other_better : !other_better;
+      if (take) { sc = os; jj = oj; }
+    }
+  // certificate
+  const float sk = __shfl(sc, (lane & 32) + top_k - 1);
+  const float ua = wa ? bucket_upper(wa) : -INFINITY;
+  const float ub = wb ? bucket_upper(wb) : -INFINITY;
+  const float e_bound = 0.0083733f * sqrtf(q2) * kmax + 1e-30f;   // 2^-6.9 |q/8| max|k|
+  const bool certified = sk > fmaxf(ua, ub) + e_bound;
+  // each of the first top_k lanes: its key's rank by index among them
+  int rank = 0;
+  for (int o = 0; o < top_k; ++o) {
+    const int oj = __shfl(jj, (lane & 32) + o);
+    rank += (oj < jj) ? 1 : 0;
+  }
+  if (!pvalid) return;
+  if (certified) {
+    if (c < top_k) {
+      idx[pr * top_k + rank] = jj;
+      if (score) score[pr * top_k + rank] = sc;
+    }
+  } else if (c == 0) {
+    const int at = atomicAdd(&fail_count[h], 1);
+    fail_rows[(long long)h * n_rows + at] = (int32_t)row;
+  }
+}
+
+// The split fallback's merge: one wave per listed block gathers the n_seg x 2
+// segment lists (n_seg / 2 entries per lane), takes the top_k by top_k rounds
+// of a wave-wide best (larger score, then lower index), and writes them in
+// ascending index order.
+constexpr int kFallbackSegs = 8;
+constexpr int kFallbackCap = 4096;  // listed rows per head taken in split mode
+
+__device__ __forceinline__ bool seg_better(float s, int j, float ts, int tj) {
+  return s > ts || (s == ts && j < tj);
+}
+
+__global__ __launch_bounds__(256) void gsa_topk_seg_merge_kernel(Geom g, int top_k, int cap,
+                                                                 const int32_t* __restrict__ rows,
+                                                                 const int32_t* __restrict__ count,
+                                                                 const float* __restrict__ seg_val,
+                                                                 const int32_t* __restrict__ seg_idx,
+                                                                 int32_t* __restrict__ idx,
+                                                                 float* __restrict__ score) {
+  constexpr int kPer = kFallbackSegs * 32 / 64;  // entries per lane
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const int lane = threadIdx.x & 63;
+  const long long wv = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int h = (int)(wv / cap);
+  const long long pos = wv % cap;
+  if (h >= g.n_heads) return;
+  const long long cnt = min((long long)count[h], (long long)cap);
+  if (pos >= cnt) return;  // (uniform over the wave)
+  const long long base = ((long long)h * cap + pos) * kFallbackSegs * 32;
+  float v[kPer];
+  int j[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    v[e] = seg_val[base + e * 64 + lane];
+    j[e] = seg_idx[base + e * 64 + lane];
+    if (j[e] == 0x7fffffff) v[e] = -INFINITY;
+  }
+  float win_v = -INFINITY;
+  int win_j = 0x7fffffff;
+  for (int k = 0; k < top_k; ++k) {
+    float bv = v[0];
+    int bj = j[0];
+#pragma unroll
+    for (int e = 1; e < kPer; ++e)
+      if (seg_better(v[e], j[e], bv, bj)) { bv = v[e]; bj = j[e]; }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const float ov = __shfl_xor(bv, sh);
+      const int oj = __shfl_xor(bj, sh);
+      if (seg_better(ov, oj, bv, bj)) { bv = ov; bj = oj; }
+    }
+    if (lane == k) { win_v = bv; win_j = bj; }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (j[e] == bj) { v[e] = -INFINITY; j[e] = 0x7fffffff; }
+  }
+  int rank = 0;
+  for (int o = 0; o < top_k; ++o) rank += (__shfl(win_j, o) < win_j) ? 1 : 0;
+  if (lane < top_k) {
+    const long long row = rows[(long long)h * n_rows + pos];
+    idx[((long long)h * n_rows + row) * top_k + rank] = win_j;
+    if (score) score[((long long)h * n_rows + row) * top_k + rank] = win_v;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // Wide selection, kRegK < top_k <= 128: bound, filter, sort.
@@ -831,7 +1273,7 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const flo
         for (int i = 0; i < 16; ++i) {
           const float sv = s[kb][i];
           const bool c = sv >= tau && sv > -INFINITY;
-          if (__any(c)) {
+          if (wave_any(c)) {
             if (c) {
               const int j = (int)u0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
               if (cnt < kWideCap) my_keys[cnt] = order_key(sv, j);
@@ -1105,7 +1547,7 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf1
       p1 += __shfl_xor(p1, 32);
       const int j = (int)u0 + kb * 32 + li;
       const float sv = (j < n_cand) ? (hh == 0 ? p0 : p1) * inv : -INFINITY;
-      if (__any(sv > tau)) {
+      if (wave_any(sv > tau)) {
         // the median insertion network of gsa_topk_reg_kernel
 #pragma unroll
         for (int p = kRegK - 1; p >= 1; --p) {
@@ -1199,7 +1641,32 @@ hipError_t launch_gsa_topk_prob(const Geom& g, const void* q, const float* k_cmp
   return hipGetLastError();
 }
 
+// The two-stage selection serves top_k <= 16 while a lane's key positions fit
+// 16 bits; its workspace: stage 1's candidate words, the key-norm partials,
+// the per-head counts and lists of blocks it could not certify.
+static bool two_stage(const Geom& g, int top_k) {
+  return top_k <= kRegK && ((long long)g.n_frames * g.nb + kTileN - 1) / kTileN <= kApproxMaxTiles;
+}
+struct TwoStageLayout {
+  int cap = 0;  // listed rows per head whose fallback is split over key segments
+  size_t cand = 0, kpart = 0, count = 0, rows = 0, seg = 0, total = 0;
+};
+static TwoStageLayout two_stage_layout(const Geom& g) {
+  TwoStageLayout l;
+  const long long n_rows = (long long)g.n_frames * g.nqb;
+  const size_t n = (size_t)n_rows * g.n_heads;
+  l.cap = (int)min((long long)kFallbackCap, (n_rows + 127) / 128 * 128);
+  l.cand = round_up256(n * 32 * sizeof(uint32_t));
+  l.kpart = round_up256((size_t)g.n_heads * kKnormChunks * sizeof(float));
+  l.count = round_up256((size_t)g.n_heads * sizeof(int32_t));
+  l.rows = round_up256(n * sizeof(int32_t));
+  l.seg = round_up256((size_t)g.n_heads * l.cap * kFallbackSegs * 32 * sizeof(float));
+  l.total = l.cand + l.kpart + l.count + l.rows + 2 * l.seg;
+  return l;
+}
+
 size_t gsa_topk_workspace(const Geom& g, int top_k) {
+  if (two_stage(g, top_k)) return planes_bytes(g) + two_stage_layout(g).total;
   if (top_k <= kRegK) return planes_bytes(g);
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const long long tiles = (n_rows + kWideRows - 1) / kWideRows * g.n_heads;
@@ -1227,16 +1694,59 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
                        g.n_heads, 1.f, static_cast<u32x4*>(planes));
     if (hipError_t e = hipGetLastError()) return e;
   }
+  if (two_stage(g, top_k)) {
+    const TwoStageLayout lay = two_stage_layout(g);
+    uint32_t* cand = reinterpret_cast<uint32_t*>(w);
+    float* kpart = reinterpret_cast<float*>(w + lay.cand);
+    int32_t* fail_count = reinterpret_cast<int32_t*>(w + lay.cand + lay.kpart);
+    int32_t* fail_rows = reinterpret_cast<int32_t*>(w + lay.cand + lay.kpart + lay.count);
+    const int n_rowtiles = (int)((n_rows + 127) / 128);
+    const long long grid = (long long)n_rowtiles * g.n_heads;
+    const long long pairs_threads = n_rows * g.n_heads * 32;
+    if (grid > 0x7fffffffLL || (pairs_threads + 255) / 256 > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kmax_partial_kernel, dim3(g.n_heads * kKnormChunks), dim3(256), 0, stream, k_cmp,
+                       n_total, g.n_heads, kpart, fail_count);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL(gsa_topk_approx_kernel, dim3((unsigned)grid), dim3(256), 2 * kTileBytes, stream, g, q_blk,
+                       planes, n_total, n_cand, first, n_rowtiles, cand);
+    if (hipError_t e = hipGetLastError()) return e;
+    hipLaunchKernelGGL(gsa_topk_rescore_kernel, dim3((unsigned)((pairs_threads + 255) / 256)), dim3(256), 0,
+                       stream, g, q_blk, k_cmp, first, top_k, cand, kpart, idx, score, fail_count, fail_rows);
+    if (hipError_t e = hipGetLastError()) return e;
+    // the blocks the certificate missed, selected again exactly: the first
+    // lay.cap per head with their keys split over kFallbackSegs workgroups
+    // (a few hundred blocks would otherwise each stream every key in one
+    // workgroup), then merged
+    const RegList fl{fail_rows, fail_count, kFallbackSegs, lay.cap,
+                     reinterpret_cast<float*>(w + lay.cand + lay.kpart + lay.count + lay.rows),
+                     reinterpret_cast<int32_t*>(w + lay.cand + lay.kpart + lay.count + lay.rows + lay.seg)};
+    const long long fgrid = grid * kFallbackSegs;
+    if (fgrid > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (top_k == kRegK) {
+      hipLaunchKernelGGL(gsa_topk_reg_kernel<true>, dim3((unsigned)fgrid), dim3(256), 2 * kStageBytes,
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score, fl);
+    } else {
+      hipLaunchKernelGGL(gsa_topk_reg_kernel<false>, dim3((unsigned)fgrid), dim3(256), 2 * kStageBytes,
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score, fl);
+    }
+    if (hipError_t e = hipGetLastError()) return e;
+    const long long mwaves = (long long)g.n_heads * lay.cap;
+    hipLaunchKernelGGL(gsa_topk_seg_merge_kernel, dim3((unsigned)((mwaves + 3) / 4)), dim3(256), 0, stream, g,
+                       top_k, lay.cap, fail_rows, fail_count, fl.seg_val, fl.seg_idx, idx, score);
+    return hipGetLastError();
+  }
   if (top_k <= kRegK) {
     const int n_rowtiles = (int)((n_rows + 127) / 128);
     const long long grid = (long long)n_rowtiles * g.n_heads;
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     if (top_k == kRegK) {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<true>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score,
+                         RegList{});
     } else {
       hipLaunchKernelGGL(gsa_topk_reg_kernel<false>, dim3((unsigned)grid), dim3(256), 2 * kStageBytes,
-                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score);
+                         stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score,
+                         RegList{});
     }
     return hipGetLastError();
   }

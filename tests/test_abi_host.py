@@ -222,7 +222,18 @@ def test_topk_workspace():
     # every width: the pooled keys split into bf16 hi/lo planes (256 bytes per
     # key and head)
     planes = r256(256 * 100 * 16 * 256)
-    assert _ws(g, 4, 16, 0) == (OK, planes)
+    # top_k <= 16 (two stages while the competing keys fill at most 2048 tiles of
+    # 64): 32 candidate words per (head, query block), 256 key-norm partial
+    # maxima per head, a count per head and a row list per head of the blocks
+    # the certificate missed, then (values and indices) the per-segment lists of
+    # the exact fallback: up to 4096 listed rows per head x 8 key segments x 32
+    two = (r256(n_rows * 16 * 32 * 4) + r256(16 * 256 * 4) + r256(16 * 4) + r256(n_rows * 16 * 4)
+           + 2 * r256(16 * 4096 * 8 * 32 * 4))
+    assert _ws(g, 4, 16, 0) == (OK, planes + two)
+    assert _ws(g, 4, 1, 2) == (OK, planes + two)
+    # past 2048 tiles (131,072 pooled keys) the exact single-stage kernel: planes only
+    big = geom(n_frames=1311)
+    assert _ws(big, 4, 16, 0) == (OK, r256(1311 * 100 * 16 * 256))
     # wider: then one 1 MiB key buffer per persistent workgroup (128 blocks x 2
     # lanes x 512 keys x 8 bytes), at most 1024 of them, then a score bound
     # (fp32) and a flag byte per (head, query block)

@@ -441,6 +441,37 @@ def test_topk_register_ties(keep_ref):
         print(f"[parity] register top-{top_k} ties (keep_ref={keep_ref}): all rows exact", flush=True)
 
 
+@pytest.mark.parametrize("top_k", [5, 16])
+def test_topk_two_stage_fallback(top_k):
+    """The two-stage selection's exact fallback at both of its sizes: with every
+    pooled key equal, no block can be certified, so all 4,848 blocks per head
+    go to the exact kernel -- the first 4,096 with their keys split over
+    segments and merged, the rest streamed whole -- and ties go to the lowest
+    indices; on the scene inputs of the same geometry the certified and the
+    fallback blocks together must match the oracle."""
+    geom = Geometry(48, 5, 37, 37, 2, 64, "bf16")
+    _announce(f"two-stage fallback top-{top_k} {geom}")
+    N, H = geom.n_frames, geom.n_heads
+    rng = np.random.default_rng(19)
+    k32 = np.tile(rng.standard_normal((1, H, 64)), (N * _nb(geom), 1, 1))
+    q32 = rng.standard_normal((N * _nqb(geom), H, 64))
+    idx, sc = sga.gsa_select_topk(torch.tensor(q32, dtype=torch.float32, device=DEV),
+                                  torch.tensor(k32, dtype=torch.float32, device=DEV), geom, top_k,
+                                  want_score=True)
+    _sync()
+    assert (host(idx).astype(np.int64) == np.arange(top_k)[None, None, :]).all()
+    s_ref = np.einsum("bhd,hd->hb", q32, k32[0]) / 8.0
+    assert np.max(np.abs(host(sc) - s_ref[:, :, None])) < 1e-4
+    q, k, v = make_qkv(geom, seed=23, device=DEV, distribution="scene")
+    _, _, k32g, q32g = sga.gsa_compress(q, k, v, geom)
+    idx_g = sga.gsa_select_topk(q32g, k32g, geom, top_k)
+    _sync()
+    rkc, _ = oracle.compress(host(k), host(v), geom, 4)
+    rqb = oracle.pooled_queries(host(q), geom, 4)
+    ridx, ranked = oracle.select_topk(rqb, rkc, top_k, workers=oracle_workers())
+    check_topk(host(idx_g).astype(np.int64), ridx, ranked, rqb, rkc, f"two-stage top-{top_k}, 48 frames")
+
+
 def test_topk_wide_few_candidates():
     """Fewer competing blocks than the bound's 128 buckets: the bound is -inf,
     every candidate is kept and sorted (3 frames x 12 blocks, top-20; 2 frames
