@@ -384,4 +384,81 @@ struct FlashWaveState {
   }
 };
 
+// Two 32-query halves per wave (64 queries) against the same staged tile:
+// every K and V^T operand read from LDS feeds both halves' MFMAs, and the two
+// halves' independent chains (one half's probabilities while the other's
+// products run on the matrix core) give the scheduler work to overlap within
+// the wave. Per half the arithmetic is FlashWaveState's, in the same order.
+struct FlashWaveState2 {
+  FlashWaveState a, b;
+
+  // Both halves start from the larger of the lane's two bounds (one register
+  // vector for both: -max(b_a, b_b) is still at least each query's logits).
+  __device__ __forceinline__ void init(float bound_a, float bound_b) {
+    const float bound = fmaxf(bound_a, bound_b);
+    a.init(bound);
+    b.init(bound);
+  }
+
+  template <bool MASKED, class MaskFn>
+  __device__ __forceinline__ void tile(const unsigned char* stage, const TileLaneOffsets& off,
+                                       const u32x4 qa[4], const u32x4 qb[4], MaskFn&& mask) {
+    f32x16 sa[2], sb[2];
+    {
+      u32x4 ka[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
+      sa[0] = mfma32(ka[0][0], qa[0], a.negm);
+      sa[1] = mfma32(ka[1][0], qa[0], a.negm);
+      sb[0] = mfma32(ka[0][0], qb[0], a.negm);
+      sb[1] = mfma32(ka[1][0], qb[0], a.negm);
+#pragma unroll
+      for (int ks = 1; ks < 4; ++ks) {
+        sa[0] = mfma32(ka[0][ks], qa[ks], sa[0]);
+        sa[1] = mfma32(ka[1][ks], qa[ks], sa[1]);
+        sb[0] = mfma32(ka[0][ks], qb[ks], sb[0]);
+        sb[1] = mfma32(ka[1][ks], qb[ks], sb[1]);
+      }
+    }
+    if constexpr (MASKED) {
+      mask(0, sa[0]);
+      mask(1, sa[1]);
+      mask(0, sb[0]);
+      mask(1, sb[1]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      u32x4 va[4];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) va[2 * db + mm] = ld16(stage + off.v_off(db, kb, mm));
+      u32x4 pa[2], pb[2];
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        float p[8], r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = fast_exp2(sa[kb][8 * mm + i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pa[mm][j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        a.l = sum_bf16x8(pa[mm], a.l);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = fast_exp2(sb[kb][8 * mm + i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pb[mm][j] = pack_bf16x2(r[2 * j], r[2 * j + 1]);
+        b.l = sum_bf16x8(pb[mm], b.l);
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          a.oacc[db] = mfma32(va[2 * db + mm], pa[mm], a.oacc[db]);
+          b.oacc[db] = mfma32(va[2 * db + mm], pb[mm], b.oacc[db]);
+        }
+    }
+  }
+};
+
 }  // namespace sga

@@ -52,21 +52,29 @@ enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
 // Measured for dense attention at 128 frames (% of bf16 peak): 4 waves x 3
 // workgroups x 3 stages 46.6; 12 x 1 x 3 (8 loading) 45.6; 8 x 1 x 5 43.2;
 // 6 x 2 x 3 38.8 (the register budget then allows only 2 waves per SIMD).
-template <int W, int G, int S, int D>
+template <int W, int G, int S, int D, int Q>
 struct TileCfg {
   static constexpr int waves = W;
   static constexpr int wg_per_cu = G;
   static constexpr int stages = S;
   static constexpr int dma_waves = D;
+  static constexpr int halves = Q;  // 32-query halves per wave
   static constexpr int threads = W * 64;
-  static constexpr int block_m = W * 32;
+  static constexpr int block_m = W * 32 * Q;
   static constexpr int rows_per_wave = 64 / D;           // K rows and V^T rows per loading wave
   static constexpr int loads_per_tile = 2 * rows_per_wave / 8;  // 16-byte loads per lane
   static_assert(D <= W && 64 % D == 0 && rows_per_wave % 8 == 0, "load split");
   static_assert(S >= 2 && S <= 9, "ring");
 };
+// GLOBAL: two 32-query halves per wave sharing every LDS operand read (64
+// queries a wave, 256 a workgroup, 2 workgroups = 2 waves per SIMD): measured
+// on a register/LDS-only probe of the tile arithmetic, 63% of the bf16 peak
+// against 51% for one half per wave at 3 waves per SIMD. FRAME/SUBSAMPLED keep
+// one half per wave (a frame's 1374 queries fill 128-query tiles better).
 template <int MODE>
-struct Cfg : TileCfg<4, 3, 3, 4> {};
+struct Cfg : TileCfg<4, 3, 3, 4, 1> {};
+template <>
+struct Cfg<0> : TileCfg<4, 2, 3, 4, 2> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -155,9 +163,7 @@ __device__ __forceinline__ void wait_and_meet() {
 // in A.redo whether some row's probabilities underflowed. EXACT = true: only the
 // recorded workgroups run, redoing their rows with the exact online softmax.
 template <int MODE, bool EXACT>
-__global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flash_bf16_kernel(
-    FlashArgs A) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+__device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned char* smem) {
   using C = Cfg<MODE>;
   constexpr int kStages = C::stages;
   constexpr int kAhead = kStages - 1;  // tiles in flight ahead of the one consumed
@@ -165,11 +171,6 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
   constexpr int kRowsPerWave = C::rows_per_wave;
   constexpr int kLoadsPerTile = C::loads_per_tile;
 
-  int lid = blockIdx.x;
-  if (A.remap) {
-    const int per = (A.n_logical + 7) >> 3;
-    lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  }
   if (lid >= A.n_logical) return;
   if (EXACT && A.redo[lid] == 0) return;
   int h, f = 0;
@@ -231,24 +232,24 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     const int kc = ld_p ^ ld_r;                               // K swizzle: chunk ^ (r & 7)
     const int vc = ld_p ^ ld_r ^ ((wave_u * (kRowsPerWave / 8) + i) & 7);  // V^T: chunk ^ swz(r)
     k_off[i] = (uint32_t)((r * rs + kc * 8) * 2);
-    v_off0[i] = (uint32_t)((r * seg0.vt_ld + vc * 8) * 2);
-    v_off1[i] = (uint32_t)((r * seg1.vt_ld + vc * 8) * 2);
+    v_off0[i] = (uint32_t)(r * 128 + vc * 16);  // V^T tiles are 64 x 64 contiguous blocks
+    v_off1[i] = v_off0[i];
   }
   // Per segment, fixed for the kernel: the byte address of this head's first K
   // row and first V^T column, the V^T extent and the key count. A tile then
   // costs one 32x32-bit product and a few adds on the scalar unit; the key and
   // byte counts fit 31 bits (checked at launch).
   const int row_bytes = (int)(rs * 2);
+  // (a head's V^T is ld / 64 tiles of 64 d-rows x 128 B: 128 B per column)
   const char* const kb0 = reinterpret_cast<const char*>(seg0.k + seg0.k_row0 * rs + hoff);
-  const char* const vb0 = reinterpret_cast<const char*>(seg0.vt + hoff * seg0.vt_ld + seg0.vt_col0);
-  const int vbytes0 = (int)(kHeadDim * seg0.vt_ld * 2), n0 = (int)seg0.n;
+  const char* const vb0 = reinterpret_cast<const char*>(seg0.vt) + (h * seg0.vt_ld + seg0.vt_col0) * 128;
+  const int n0 = (int)seg0.n;
   const char* kb1 = kb0;
   const char* vb1 = vb0;
-  int vbytes1 = vbytes0, n1 = n0;
+  int n1 = n0;
   if (MODE == MODE_SUBSAMPLED) {
     kb1 = reinterpret_cast<const char*>(seg1.k + seg1.k_row0 * rs + hoff);
-    vb1 = reinterpret_cast<const char*>(seg1.vt + hoff * seg1.vt_ld + seg1.vt_col0);
-    vbytes1 = (int)(kHeadDim * seg1.vt_ld * 2);
+    vb1 = reinterpret_cast<const char*>(seg1.vt) + (h * seg1.vt_ld + seg1.vt_col0) * 128;
     n1 = (int)seg1.n;
   }
   auto issue_tile = [&](int j, unsigned char* stage) {
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     const int u0 = (second ? j - nt0 : j) * kTileKeys;
     const int rows = min(kTileKeys, (second ? n1 : n0) - u0);
     const auto kr = buffer_rsrc((second ? kb1 : kb0) + (long long)u0 * row_bytes, rows * row_bytes);
-    const auto vr = buffer_rsrc((second ? vb1 : vb0) + 2LL * u0, second ? vbytes1 : vbytes0);
+    const auto vr = buffer_rsrc((second ? vb1 : vb0) + (long long)u0 * 128, kTileVBytes);
     unsigned char* kdst = stage + wave_u * kRowsPerWave * 128;
     unsigned char* vdst = kdst + kTileKBytes;
     if (C::dma_waves < C::waves && wave_u >= C::dma_waves) return;
@@ -346,10 +347,16 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     }
   };
 
-  const long long qrow = q0 + wave * 32 + li;
-  const bool qvalid = qrow < q_end;
-  u32x4 qB[4];
-  load_q_operand_scaled(A.q + (qvalid ? qrow : q0) * rs + hoff, qvalid, c, qB);
+  constexpr int kHalves = C::halves;
+  long long qrow[kHalves];
+  bool qvalid[kHalves];
+  u32x4 qB[kHalves][4];
+#pragma unroll
+  for (int hq = 0; hq < kHalves; ++hq) {
+    qrow[hq] = q0 + (wave * kHalves + hq) * 32 + li;
+    qvalid[hq] = qrow[hq] < q_end;
+    load_q_operand_scaled(A.q + (qvalid[hq] ? qrow[hq] : q0) * rs + hoff, qvalid[hq], c, qB[hq]);
+  }
 
   TileLaneOffsets off;
   off.init();
@@ -402,20 +409,29 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
       step(tile_of(j), smem + cur * kStageBytes);
     }
   };
-  bf16* orow = A.o + qrow * rs + hoff;
-  float* lse_ptr = A.lse ? A.lse + qrow * A.g.n_heads + h : nullptr;
+  bf16* orow[kHalves];
+  float* lse_ptr[kHalves];
+#pragma unroll
+  for (int hq = 0; hq < kHalves; ++hq) {
+    orow[hq] = A.o + qrow[hq] * rs + hoff;
+    lse_ptr[hq] = A.lse ? A.lse + qrow[hq] * A.g.n_heads + h : nullptr;
+  }
   if constexpr (EXACT) {
     // scores already in log2 units, so c = 1
-    WaveAttnState ex;
-    ex.init();
+    WaveAttnState ex[kHalves];
+#pragma unroll
+    for (int hq = 0; hq < kHalves; ++hq) ex[hq].init();
     auto step = [&](int t, const unsigned char* stage, bool masked) {
-      f32x16 sc[2];
-      ex.scores(stage, off, qB, sc);
-      if (masked) {
-        apply_mask(t, 0, sc[0]);
-        apply_mask(t, 1, sc[1]);
+#pragma unroll
+      for (int hq = 0; hq < kHalves; ++hq) {
+        f32x16 sc[2];
+        ex[hq].scores(stage, off, qB[hq], sc);
+        if (masked) {
+          apply_mask(t, 0, sc[0]);
+          apply_mask(t, 1, sc[1]);
+        }
+        ex[hq].consume(sc, stage, off, 1.f, false, true);
       }
-      ex.consume(sc, stage, off, 1.f, false, true);
     };
     for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
@@ -425,47 +441,86 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
       }
     }
     run_rest([&](int t, const unsigned char* stage) { step(t, stage, true); });
-    ex.finish(orow, lse_ptr, qvalid, 1.f);
+#pragma unroll
+    for (int hq = 0; hq < kHalves; ++hq) ex[hq].finish(orow[hq], lse_ptr[hq], qvalid[hq], 1.f);
   } else {
     // Upper bound of the query's logits (log2 units): |q'| max|k| with a margin
     // for the rounding of |q'|, of max|k| and of the bf16 mean keys, plus the
     // mean rows' bias. The key-norm partials are per (head, chunk) maxima of |k|^2.
-    float bound;
+    float bound[kHalves];
     {
-      float q2 = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float a0 = lo_bf16(qB[ks][jj]), a1 = hi_bf16(qB[ks][jj]);
-          q2 = fmaf(a0, a0, fmaf(a1, a1, q2));
-        }
-      q2 = sum_halves(q2);
       float k2 = 0.f;
       for (int i = lane; i < kNormChunks; i += 64) k2 = fmaxf(k2, A.knorm2[h * kNormChunks + i]);
 #pragma unroll
       for (int sh = 32; sh >= 1; sh >>= 1) k2 = fmaxf(k2, __shfl_xor(k2, sh));
-      bound = sqrtf(q2) * sqrtf(k2) * kBoundMargin + A.bound_extra;
-    }
-    FlashWaveState st;
-    st.init(bound);
-    for (int j = 0; j < n_main; j += kStages) {
 #pragma unroll
-      for (int cur = 0; cur < kStages; ++cur) {
-        enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
-        st.tile<false>(smem + cur * kStageBytes, off, qB, [](int, f32x16&) {});
+      for (int hq = 0; hq < kHalves; ++hq) {
+        float q2 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float a0 = lo_bf16(qB[hq][ks][jj]), a1 = hi_bf16(qB[hq][ks][jj]);
+            q2 = fmaf(a0, a0, fmaf(a1, a1, q2));
+          }
+        q2 = sum_halves(q2);
+        bound[hq] = sqrtf(q2) * sqrtf(k2) * kBoundMargin + A.bound_extra;
       }
     }
-    run_rest([&](int t, const unsigned char* stage) {
-      st.tile<true>(stage, off, qB, [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
-    });
     // A bound far above a row's true maximum leaves its probabilities below
     // the fp32 range: the workgroup is then redone by the exact pass.
-    const bool loose = !(sum_halves(st.l) >= kLooseBoundSum);
+    bool loose = false;
+    if constexpr (kHalves == 1) {
+      FlashWaveState st;
+      st.init(bound[0]);
+      for (int j = 0; j < n_main; j += kStages) {
+#pragma unroll
+        for (int cur = 0; cur < kStages; ++cur) {
+          enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+          st.tile<false>(smem + cur * kStageBytes, off, qB[0], [](int, f32x16&) {});
+        }
+      }
+      run_rest([&](int t, const unsigned char* stage) {
+        st.tile<true>(stage, off, qB[0], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
+      });
+      loose = !(sum_halves(st.l) >= kLooseBoundSum);
+      st.finish(orow[0], lse_ptr[0], qvalid[0]);
+    } else {
+      FlashWaveState2 st;
+      st.init(bound[0], bound[1]);
+      for (int j = 0; j < n_main; j += kStages) {
+#pragma unroll
+        for (int cur = 0; cur < kStages; ++cur) {
+          enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+          st.tile<false>(smem + cur * kStageBytes, off, qB[0], qB[1], [](int, f32x16&) {});
+        }
+      }
+      run_rest([&](int t, const unsigned char* stage) {
+        st.tile<true>(stage, off, qB[0], qB[1], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
+      });
+      loose = !(sum_halves(st.a.l) >= kLooseBoundSum) || !(sum_halves(st.b.l) >= kLooseBoundSum);
+      st.a.finish(orow[0], lse_ptr[0], qvalid[0]);
+      st.b.finish(orow[1], lse_ptr[1], qvalid[1]);
+    }
     const int any_loose = __syncthreads_or(loose);
     if (tid == 0) A.redo[lid] = any_loose ? 1 : 0;
-    st.finish(orow, lse_ptr, qvalid);
   }
+}
+
+// The kernel: one workgroup per logical workgroup (remapped per XCD in
+// FRAME/SUBSAMPLED mode). A persistent grid that keeps the resident
+// workgroups streaming the same keys in step was measured slower at every
+// size (1000 frames: 43.8-45.8% of the bf16 peak against 48-49%).
+template <int MODE, bool EXACT>
+__global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flash_bf16_kernel(
+    FlashArgs A) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int lid = blockIdx.x;
+  if (A.remap) {
+    const int per = (A.n_logical + 7) >> 3;
+    lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  }
+  flash_tile<MODE, EXACT>(A, lid, smem);
 }
 
 // Per (head, chunk) maximum of |k|^2 over the rows of K: a workgroup per

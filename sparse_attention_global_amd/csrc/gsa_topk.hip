@@ -1310,23 +1310,6 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_wide_kernel(Geom g, const flo
 }
 
 // Workgroups of a kernel that fit on the device at once.
-int resident_workgroups(const void* kernel, int threads, size_t lds) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  static int cus[64] = {0};
-  int n_cu = 256;
-  if (dev >= 0 && dev < 64) {
-    if (cus[dev] == 0) {
-      hipDeviceProp_t prop;
-      if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus[dev] = prop.multiProcessorCount;
-    }
-    if (cus[dev] > 0) n_cu = cus[dev];
-  }
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  return per_cu * n_cu;
-}
 
 // ---------------------------------------------------------------------------
 // Probability-mean block scores (the block score read as probabilities: the
@@ -1588,6 +1571,25 @@ __global__ __launch_bounds__(256, 3) void gsa_topk_prob_kernel(Geom g, const bf1
 }
 
 }  // namespace
+
+// Workgroups of `kernel` the device holds at once (occupancy x compute units).
+int resident_workgroups(const void* kernel, int threads, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cus[64] = {0};
+  int n_cu = 256;
+  if (dev >= 0 && dev < 64) {
+    if (cus[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus[dev] = prop.multiProcessorCount;
+    }
+    if (cus[dev] > 0) n_cu = cus[dev];
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return per_cu * n_cu;
+}
 
 static size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 

@@ -32,6 +32,10 @@ struct FlashLaunch {
   int s_h, s_w;      // SUBSAMPLED, token_diag (fp32): the strides, to find dropped queries
 };
 
+// Workgroups of `kernel` (threads per workgroup, dynamic LDS bytes) that the
+// current device holds resident at once: occupancy per CU times the CU count.
+int resident_workgroups(const void* kernel, int threads, size_t lds);
+
 // bf16 MFMA flash attention (flash_bf16.hip). ws holds the V^T staging of the
 // values (and of the compacted values in SUBSAMPLED mode), the key-norm
 // partials and the redo flags; its size is flash_bf16_workspace(p).

@@ -1,7 +1,10 @@
 // V^T staging for the bf16 attention kernels: one pass that rewrites a value
-// tensor [rows, H, 64] as, per head, 64 rows of d holding the keys as columns,
-//   vt[(h * 64 + d) * ld + col] = V[key(col), h, d]   (0 where col holds no key),
-// in the column order the MFMA B operand wants: inside every 16-column group,
+// tensor [rows, H, 64] as, per head and 64-column tile, 64 rows of d holding the
+// tile's keys as columns (each tile one contiguous 8 KiB block, so a tile load
+// touches one or two memory pages, whatever the key count),
+//   vt[((h * (ld / 64) + col / 64) * 64 + d) * 64 + col % 64] = V[key(col), h, d]
+// (0 where col holds no key), in the column order the MFMA B operand wants:
+// inside every 16-column group,
 // column 8hh + 4a + r holds key offset 8a + 4hh + r (bits 2 and 3 swapped; the
 // map is its own inverse). Keys may be grouped in segments of seg_len padded to
 // seg_pad columns (seg_pad a multiple of 64), so every segment (a frame) starts
@@ -55,7 +58,7 @@ __global__ __launch_bounds__(256) void vt_prepare_kernel(const bf16* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w[j] = (uint32_t)tile[cc * 8 + 2 * j][d] | ((uint32_t)tile[cc * 8 + 2 * j + 1][d] << 16);
-    st16(vt + ((long long)h * kHeadDim + d) * ld + col0 + cc * 8, w);
+    st16(vt + (((long long)h * n_ctiles + col0 / 64) * kHeadDim + d) * 64 + cc * 8, w);
   }
 }
 
