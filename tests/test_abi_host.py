@@ -160,9 +160,9 @@ def test_workspace_sizes():
     T = 256 * 1374
     # dense bf16: V^T staging, keys rounded up to 64 columns, 16 heads x 64 rows
     # of d, then 256 key-norm partial maxima per head (fp32), then one redo flag
-    # byte per workgroup of 128 queries
+    # byte per workgroup of 256 queries
     norms = 16 * 256 * 4
-    flags = r256(-(-T // 128) * 16)
+    flags = r256(-(-T // 256) * 16)
     assert _ws(g, 2, 0, 0) == (OK, 16 * 64 * ((T + 63) // 64 * 64) * 2 + norms + flags)
     assert _ws(g, 2, 25600, 0) == (OK, 16 * 64 * 25600 * 2 + norms + flags)
     # frame mode: every frame padded to 1408 columns, 11 workgroups per frame
@@ -191,9 +191,9 @@ def test_fine_workspace():
     def expect(rows):
         # the kept tokens' gathered K and V, the queries' log-sum-exp over them,
         # and the dense staging for those keys (V^T, key-norm partials, one redo
-        # flag per 128-query workgroup)
+        # flag per 256-query workgroup)
         kv = r256(rows * 16 * 64 * 2)
-        flash = r256(16 * 64 * ((rows + 63) // 64 * 64) * 2 + 16 * 256 * 4 + r256(-(-T // 128) * 16))
+        flash = r256(16 * 64 * ((rows + 63) // 64 * 64) * 2 + 16 * 256 * 4 + r256(-(-T // 256) * 16))
         return 2 * kv + lse + flash
 
     # special tokens only: 256 frames x 5
@@ -278,9 +278,9 @@ def test_pooled_workspace():
     nq = 256 * 101
     # bf16: the pooled queries in bf16, the per-block outputs, and the dense
     # staging over the 25,600 pooled keys (V^T, key-norm partials, one redo flag
-    # per 128-query workgroup)
+    # per 256-query workgroup)
     blk = r256(nq * 16 * 64 * 2)
-    flash = r256(16 * 64 * 25600 * 2 + 16 * 256 * 4 + r256(-(-nq // 128) * 16))
+    flash = r256(16 * 64 * 25600 * 2 + 16 * 256 * 4 + r256(-(-nq // 256) * 16))
     assert _ws(g, 5, 0, 0) == (OK, 2 * blk + flash)
     # fp32: the per-block outputs only
     assert _ws(geom(n_frames=3, dtype=1), 5, 0, 0) == (OK, r256(3 * 101 * 16 * 64 * 4))
