@@ -208,8 +208,11 @@ sga_status gsa_gate(const sga_geom* geom, const void* q, const void* o_cmp,
  * GSA fine attention with the gated aggregation folded in (Speed3R section
  * 2.1, selection branch then gated aggregation; the single fused pass of
  * Speed3R section 2.2 takes the gate into the selection branch's epilogue):
- * O = g0 * o_cmp + g1 * (gsa_sparse_attn's result), g as in gsa_gate, with the
- * fine result taken before it is rounded to the I/O type. Same arguments and
+ * O = g0 * o_cmp + g1 * (gsa_sparse_attn's result), g as in gsa_gate. The
+ * fine result enters the gate unrounded, except that with a non-empty kept set
+ * in bf16 the kept tokens' partial result (normalised, from the dense kernel)
+ * is rounded to bf16 once before the selected windows continue its softmax,
+ * exactly as in gsa_sparse_attn. Same arguments and
  * workspace as gsa_sparse_attn, plus o_cmp [T, H, d] (the compressed branch
  * output), w_gate [H, 2, d] fp32 and b_gate [H, 2] fp32; the fine branch's
  * output and log-sum-exp are not stored. o must not alias o_cmp (an error).
