@@ -147,6 +147,23 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
                            void* stream);
 
 /*
+ * gsa_select_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, results and errors as
+ * gsa_select_topk; its scratch is a file-scope device array of
+ * SGA_NOALLOC_SCRATCH_BYTES per GPU, held by the library until the process
+ * ends. A problem whose selection scratch does not fit returns
+ * SGA_ERR_UNSUPPORTED (for top_k <= 16 and 16 heads, up to about 20,000 pooled
+ * blocks). Every call on one GPU uses that GPU's single array: calls that
+ * overlap in time on the same GPU (other streams, other threads) race and
+ * must be serialised by the caller. Nothing is allocated or freed.
+ */
+#define SGA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+sga_status gsa_select_topk_noalloc(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                                   const float* k_cmp_f32, int32_t top_k, int32_t keep,
+                                   int32_t* idx, float* score, void* stream);
+
+/*
  * GSA block selection with probability-mean block scores (the alternative
  * reading of the selection branch's block score, Speed3R section 2.1: the
  * attention of the compressed branch guides the selection): the score of

@@ -31,6 +31,7 @@ SGA_KEEP_SPECIAL = 1
 SGA_KEEP_REF_FRAME = 2
 
 EXPORTS = ("dense_global_attn", "gsa_compress", "gsa_compressed_pooled", "gsa_select_topk",
+           "gsa_select_topk_noalloc",
            "gsa_select_topk_probability",
            "gsa_sparse_attn", "gsa_sparse_attn_gated", "gsa_gate",
            "sga_compact", "subsampled_global_attn", "sga_workspace_size", "sga_last_error",
@@ -59,6 +60,7 @@ def library() -> ctypes.CDLL:
         "gsa_compress": [G, I32, I32, P, P, P, P, P, P, P, P],
         "gsa_compressed_pooled": [G, I32, P, P, P, P, P, SZ, P],
         "gsa_select_topk": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
+        "gsa_select_topk_noalloc": [G, I32, P, P, I32, I32, P, P, P],
         "gsa_select_topk_probability": [G, I32, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn": [G, I32, P, P, P, P, I32, I32, P, P, P, SZ, P],
         "gsa_sparse_attn_gated": [G, I32, P, P, P, P, I32, I32, P, P, P, P, P, SZ, P],
@@ -248,6 +250,25 @@ def gsa_select_topk(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
                                      _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                      _stream(q_blk_f32)),
            "gsa_select_topk")
+    return (idx, score) if want_score else idx
+
+
+def gsa_select_topk_noalloc(q_blk_f32, k_cmp_f32, geom, top_k: int, block: int = 4,
+                            want_score: bool = False, dtype_code: int = SGA_BF16, keep_ref: bool = False):
+    """gsa_select_topk on the library's own per-GPU scratch (no workspace; the
+    outputs are still allocated here); see include/sga.h."""
+    H, d, N = geom.n_heads, 64, geom.n_frames
+    nb, nqb = pooled_shape(geom, block)
+    _need(q_blk_f32, "q_blk_f32", N * nqb, H, d, torch.float32)
+    _need(k_cmp_f32, "k_cmp_f32", N * nb, H, d, torch.float32)
+    idx = torch.empty((H, N * nqb, top_k), dtype=torch.int32, device=q_blk_f32.device)
+    score = torch.empty((H, N * nqb, top_k), dtype=torch.float32,
+                        device=q_blk_f32.device) if want_score else None
+    g = make_geom(geom, dtype_code)
+    _check(library().gsa_select_topk_noalloc(ctypes.byref(g), block, _ptr(q_blk_f32), _ptr(k_cmp_f32), top_k,
+                                             keep_flags(False, keep_ref), _ptr(idx), _ptr(score),
+                                             _stream(q_blk_f32)),
+           "gsa_select_topk_noalloc")
     return (idx, score) if want_score else idx
 
 

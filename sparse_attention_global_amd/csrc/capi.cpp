@@ -308,6 +308,29 @@ sga_status gsa_select_topk(const sga_geom* geom, int32_t block, const float* q_b
                   "gsa_select_topk launch");
 }
 
+sga_status gsa_select_topk_noalloc(const sga_geom* geom, int32_t block, const float* q_blk_f32,
+                                   const float* k_cmp_f32, int32_t top_k, int32_t keep, int32_t* idx,
+                                   float* score, void* stream) {
+  sga::Geom g;
+  if (sga_status st = make_geom(geom, &g)) return st;
+  if (sga_status st = check_block(block)) return st;
+  if (sga_status st = check_topk(g, top_k, keep)) return st;
+  REQUIRE_PTR(q_blk_f32);
+  REQUIRE_PTR(k_cmp_f32);
+  REQUIRE_PTR(idx);
+  REQUIRE_OPT_PTR(score);
+  const int cap = sga::gsa_topk_split_cap(g, top_k, sga::kNoAllocScratchBytes);
+  if (cap < 0)
+    return fail(SGA_ERR_UNSUPPORTED,
+                "gsa_select_topk_noalloc: the selection needs %zu bytes of scratch, more than the %zu bytes it holds",
+                sga::gsa_topk_workspace(g, top_k, 0), sga::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (hipError_t e = sga::noalloc_scratch(&ws)) return from_hip(e, "gsa_select_topk_noalloc scratch lookup");
+  return from_hip(sga::launch_gsa_topk(g, q_blk_f32, k_cmp_f32, top_k, first_candidate(g, keep), idx, score, ws,
+                                       static_cast<hipStream_t>(stream), cap),
+                  "gsa_select_topk_noalloc launch");
+}
+
 // The fine branch into `out`; with gate, its gated aggregation with o_cmp.
 static sga_status sparse_attn(const sga_geom* geom, int32_t block, const void* q, const void* k,
                               const void* v, const int32_t* idx, int32_t top_k, int32_t keep,

@@ -26,6 +26,8 @@
 //   its fallback:    sorted per-block lists in LDS, inserted one half-wave at
 //                    a time (gsa_topk_kernel), for the blocks the filter
 //                    could not hold.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1653,11 +1655,13 @@ struct TwoStageLayout {
   int cap = 0;  // listed rows per head whose fallback is split over key segments
   size_t cand = 0, kpart = 0, count = 0, rows = 0, seg = 0, total = 0;
 };
-static TwoStageLayout two_stage_layout(const Geom& g) {
+// cap: listed rows per head whose fallback is split (a multiple of 128; the
+// rest stream every key in one workgroup)
+static TwoStageLayout two_stage_layout(const Geom& g, int cap = kFallbackCap) {
   TwoStageLayout l;
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const size_t n = (size_t)n_rows * g.n_heads;
-  l.cap = (int)min((long long)kFallbackCap, (n_rows + 127) / 128 * 128);
+  l.cap = (int)min((long long)cap, (n_rows + 127) / 128 * 128);
   l.cand = round_up256(n * 32 * sizeof(uint32_t));
   l.kpart = round_up256((size_t)g.n_heads * kKnormChunks * sizeof(float));
   l.count = round_up256((size_t)g.n_heads * sizeof(int32_t));
@@ -1667,8 +1671,10 @@ static TwoStageLayout two_stage_layout(const Geom& g) {
   return l;
 }
 
-size_t gsa_topk_workspace(const Geom& g, int top_k) {
-  if (two_stage(g, top_k)) return planes_bytes(g) + two_stage_layout(g).total;
+size_t gsa_topk_workspace(const Geom& g, int top_k) { return gsa_topk_workspace(g, top_k, kFallbackCap); }
+
+size_t gsa_topk_workspace(const Geom& g, int top_k, int cap) {
+  if (two_stage(g, top_k)) return planes_bytes(g) + two_stage_layout(g, cap).total;
   if (top_k <= kRegK) return planes_bytes(g);
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const long long tiles = (n_rows + kWideRows - 1) / kWideRows * g.n_heads;
@@ -1678,8 +1684,20 @@ size_t gsa_topk_workspace(const Geom& g, int top_k) {
          round_up256((size_t)(n_rows * g.n_heads));
 }
 
+int gsa_topk_split_cap(const Geom& g, int top_k, size_t bytes) {
+  if (!two_stage(g, top_k)) return gsa_topk_workspace(g, top_k) <= bytes ? kFallbackCap : -1;
+  for (int cap = kFallbackCap; cap >= 0; cap -= 128)
+    if (gsa_topk_workspace(g, top_k, cap) <= bytes) return cap;
+  return -1;
+}
+
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
                            int first, int32_t* idx, float* score, void* ws, hipStream_t stream) {
+  return launch_gsa_topk(g, q_blk, k_cmp, top_k, first, idx, score, ws, stream, kFallbackCap);
+}
+
+hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
+                           int first, int32_t* idx, float* score, void* ws, hipStream_t stream, int cap) {
   const long long n_rows = (long long)g.n_frames * g.nqb;
   const long long n_total = (long long)g.n_frames * g.nb;
   // the kernels see the competing keys only, indexed from 0, and add `first`
@@ -1697,7 +1715,7 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
     if (hipError_t e = hipGetLastError()) return e;
   }
   if (two_stage(g, top_k)) {
-    const TwoStageLayout lay = two_stage_layout(g);
+    const TwoStageLayout lay = two_stage_layout(g, cap);
     uint32_t* cand = reinterpret_cast<uint32_t*>(w);
     float* kpart = reinterpret_cast<float*>(w + lay.cand);
     int32_t* fail_count = reinterpret_cast<int32_t*>(w + lay.cand + lay.kpart);
@@ -1787,6 +1805,32 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
   hipLaunchKernelGGL(gsa_topk_kernel, dim3((unsigned)lds_grid), dim3(64 * waves), lds_for(waves), stream,
                      g, q_blk, kc, n_cand, first, top_k, n_lds_tiles, flags, idx, score);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free selection entry point: one file-scope device
+// array per GPU the library runs on, held until the process ends. Host code
+// never passes the array's name to a kernel (on the host it is only a stand-in
+// for the symbol): its device address is looked up once per device, with that
+// device current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace sga

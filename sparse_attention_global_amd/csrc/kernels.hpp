@@ -79,6 +79,11 @@ inline long long kept_rows(const Geom& g, int keep) {
 // (the wide selection's per-workgroup key buffers and overflow flags; none
 // for top_k <= 16).
 size_t gsa_topk_workspace(const Geom& g, int top_k);
+// The same with the split-fallback capacity `cap` (listed rows per head, a
+// multiple of 128; launch_gsa_topk must get the same value), and the largest
+// such capacity whose workspace fits `bytes` (-1: none fits).
+size_t gsa_topk_workspace(const Geom& g, int top_k, int cap);
+int gsa_topk_split_cap(const Geom& g, int top_k, size_t bytes);
 // Probability-mean block scores (gsa_topk.hip): top-K (<= 16) per (head, query
 // block) of the mean over the block's tokens of their compressed softmax
 // probabilities (q bf16 [T, H, d]); keys j >= first compete, every pooled key
@@ -89,6 +94,14 @@ hipError_t launch_gsa_topk_prob(const Geom& g, const void* q, const float* k_cmp
                                 int32_t* idx, float* score, void* ws, hipStream_t stream);
 hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
                            int first, int32_t* idx, float* score, void* ws, hipStream_t stream);
+hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp, int top_k,
+                           int first, int32_t* idx, float* score, void* ws, hipStream_t stream, int cap);
+// The allocation-free selection's scratch: a file-scope device array of
+// kNoAllocScratchBytes per GPU (gsa_topk.hip); noalloc_scratch gives its
+// device address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t noalloc_scratch(void** ptr);
 
 // GSA fine attention (gsa_fine.hip); bf16 MFMA or fp32. keep: kKeep* flags.
 // fp32 visits the kept tokens itself. bf16 takes them through o_init/lse_init
