@@ -52,19 +52,21 @@ enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
 // Measured for dense attention at 128 frames (% of bf16 peak): 4 waves x 3
 // workgroups x 3 stages 46.6; 12 x 1 x 3 (8 loading) 45.6; 8 x 1 x 5 43.2;
 // 6 x 2 x 3 38.8 (the register budget then allows only 2 waves per SIMD).
-template <int W, int G, int S, int D, int Q>
+template <int W, int G, int S, int D, int Q, bool P = false>
 struct TileCfg {
   static constexpr int waves = W;
   static constexpr int wg_per_cu = G;
   static constexpr int stages = S;
   static constexpr int dma_waves = D;
   static constexpr int halves = Q;  // 32-query halves per wave
+  static constexpr bool pairs = P;  // 4 stages refilled two at a time, one barrier per two tiles
   static constexpr int threads = W * 64;
   static constexpr int block_m = W * 32 * Q;
   static constexpr int rows_per_wave = 64 / D;           // K rows and V^T rows per loading wave
   static constexpr int loads_per_tile = 2 * rows_per_wave / 8;  // 16-byte loads per lane
   static_assert(D <= W && 64 % D == 0 && rows_per_wave % 8 == 0, "load split");
   static_assert(S >= 2 && S <= 9, "ring");
+  static_assert(!P || S == 4, "pairs of tiles use a 4-stage ring");
 };
 // GLOBAL: two 32-query halves per wave sharing every LDS operand read (64
 // queries a wave, 256 a workgroup, 2 workgroups = 2 waves per SIMD): measured
@@ -74,7 +76,7 @@ struct TileCfg {
 template <int MODE>
 struct Cfg : TileCfg<4, 3, 3, 4, 1> {};
 template <>
-struct Cfg<0> : TileCfg<4, 2, 3, 4, 2> {};
+struct Cfg<0> : TileCfg<4, 2, 4, 4, 2, true> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -362,10 +364,8 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
   off.init();
 
   // The tile loop: a ring of kStages LDS stages, kAhead tiles in flight, in
-  // the order tile_of(0), tile_of(1), ...
-#pragma unroll
-  for (int j = 0; j < kAhead; ++j)
-    if (j < n_tiles) issue_tile(tile_of(j), smem + j * kStageBytes);
+  // the order tile_of(0), tile_of(1), ... (the ring's first loads are issued by
+  // drive below)
   // wait for tile j (the tiles after it in flight: min(kAhead - 1, left)), meet
   // the other waves (all done with tile j - 1's stage), refill that stage
   // (waves that issue no loads have nothing outstanding: every wait passes)
@@ -409,6 +409,53 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
       step(tile_of(j), smem + cur * kStageBytes);
     }
   };
+  // The whole key stream: clean(stage) for each tile of the main rounds (all
+  // clean), rest(t, stage) for tile t of the others.
+  //   ring:  kAhead tiles in flight; one wait and barrier per tile.
+  //   pairs: stages {0,1} and {2,3} alternate; at each barrier (every second
+  //          tile) the pair just freed is refilled with the tiles two ahead,
+  //          whose loads then have two tiles' time to land (as in a 3-stage
+  //          ring) -- half the barriers, for 4 stages of LDS.
+  auto drive = [&](auto&& clean, auto&& rest) {
+    if constexpr (!C::pairs) {
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j)
+        if (j < n_tiles) issue_tile(tile_of(j), smem + j * kStageBytes);
+      for (int j = 0; j < n_main; j += kStages) {
+#pragma unroll
+        for (int cur = 0; cur < kStages; ++cur) {
+          enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
+          clean(smem + cur * kStageBytes);
+        }
+      }
+      run_rest(rest);
+    } else {
+      if (0 < n_tiles) issue_tile(tile_of(0), smem);
+      if (1 < n_tiles) issue_tile(tile_of(1), smem + kStageBytes);
+      // main rounds of 4 clean tiles; every tile issued ahead is clean too
+      const int n_main_p = max(0, n_clean - 2) / 4 * 4;
+      for (int j = 0; j < n_main_p; j += 4) {
+        wait_and_meet<0>();
+        issue_tile(clean_tile(j + 2), smem + 2 * kStageBytes);
+        issue_tile(clean_tile(j + 3), smem + 3 * kStageBytes);
+        clean(smem);
+        clean(smem + kStageBytes);
+        wait_and_meet<0>();
+        issue_tile(clean_tile(j + 4), smem);
+        issue_tile(clean_tile(j + 5), smem + kStageBytes);
+        clean(smem + 2 * kStageBytes);
+        clean(smem + 3 * kStageBytes);
+      }
+      for (int j = n_main_p; j < n_tiles; j += 2) {
+        wait_and_meet<0>();
+        const int sj = j & 3;  // 0 or 2: the pair's first stage
+        if (j + 2 < n_tiles) issue_tile(tile_of(j + 2), smem + ((sj + 2) & 3) * kStageBytes);
+        if (j + 3 < n_tiles) issue_tile(tile_of(j + 3), smem + ((sj + 3) & 3) * kStageBytes);
+        rest(tile_of(j), smem + sj * kStageBytes);
+        if (j + 1 < n_tiles) rest(tile_of(j + 1), smem + (sj + 1) * kStageBytes);
+      }
+    }
+  };
   bf16* orow[kHalves];
   float* lse_ptr[kHalves];
 #pragma unroll
@@ -433,14 +480,8 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
         ex[hq].consume(sc, stage, off, 1.f, false, true);
       }
     };
-    for (int j = 0; j < n_main; j += kStages) {
-#pragma unroll
-      for (int cur = 0; cur < kStages; ++cur) {
-        enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
-        step(clean_tile(j + cur), smem + cur * kStageBytes, false);
-      }
-    }
-    run_rest([&](int t, const unsigned char* stage) { step(t, stage, true); });
+    drive([&](const unsigned char* stage) { step(0, stage, false); },
+          [&](int t, const unsigned char* stage) { step(t, stage, true); });
 #pragma unroll
     for (int hq = 0; hq < kHalves; ++hq) ex[hq].finish(orow[hq], lse_ptr[hq], qvalid[hq], 1.f);
   } else {
@@ -473,31 +514,19 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
     if constexpr (kHalves == 1) {
       FlashWaveState st;
       st.init(bound[0]);
-      for (int j = 0; j < n_main; j += kStages) {
-#pragma unroll
-        for (int cur = 0; cur < kStages; ++cur) {
-          enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
-          st.tile<false>(smem + cur * kStageBytes, off, qB[0], [](int, f32x16&) {});
-        }
-      }
-      run_rest([&](int t, const unsigned char* stage) {
-        st.tile<true>(stage, off, qB[0], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
-      });
+      drive([&](const unsigned char* stage) { st.tile<false>(stage, off, qB[0], [](int, f32x16&) {}); },
+            [&](int t, const unsigned char* stage) {
+              st.tile<true>(stage, off, qB[0], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
+            });
       loose = !(sum_halves(st.l) >= kLooseBoundSum);
       st.finish(orow[0], lse_ptr[0], qvalid[0]);
     } else {
       FlashWaveState2 st;
       st.init(bound[0], bound[1]);
-      for (int j = 0; j < n_main; j += kStages) {
-#pragma unroll
-        for (int cur = 0; cur < kStages; ++cur) {
-          enter_clean(j + cur, smem + ((cur + kAhead) % kStages) * kStageBytes);
-          st.tile<false>(smem + cur * kStageBytes, off, qB[0], qB[1], [](int, f32x16&) {});
-        }
-      }
-      run_rest([&](int t, const unsigned char* stage) {
-        st.tile<true>(stage, off, qB[0], qB[1], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
-      });
+      drive([&](const unsigned char* stage) { st.tile<false>(stage, off, qB[0], qB[1], [](int, f32x16&) {}); },
+            [&](int t, const unsigned char* stage) {
+              st.tile<true>(stage, off, qB[0], qB[1], [&](int kb, f32x16& s) { apply_mask(t, kb, s); });
+            });
       loose = !(sum_halves(st.a.l) >= kLooseBoundSum) || !(sum_halves(st.b.l) >= kLooseBoundSum);
       st.a.finish(orow[0], lse_ptr[0], qvalid[0]);
       st.b.finish(orow[1], lse_ptr[1], qvalid[1]);
