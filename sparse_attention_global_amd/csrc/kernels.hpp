@@ -43,7 +43,8 @@ int resident_workgroups(const void* kernel, int threads, size_t lds);
 size_t flash_bf16_workspace(const FlashLaunch& p);
 bool flash_bf16_fits(const FlashLaunch& p);
 hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream);
-// V^T staging (vt_prepare.hip): vt[(h*64 + d)*ld + col] = v[key(col), h, d], keys
+// V^T staging (vt_prepare.hip), tile-major: head h's 64-column tile t is the
+// 64 x 64 block vt[((h*(ld/64) + t)*64 + d)*64 + c] = v[key(64t + c), h, d], keys
 // in segments of seg_len padded to seg_pad columns, MFMA key order in 16-column groups.
 hipError_t launch_vt_prepare(const void* v, int n_heads, long long n_rows, long long seg_len,
                              long long seg_pad, long long ld, void* vt, hipStream_t stream);
