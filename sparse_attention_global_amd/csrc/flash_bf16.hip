@@ -52,31 +52,35 @@ enum { MODE_GLOBAL = 0, MODE_FRAME = 1, MODE_SUBSAMPLED = 2 };
 // Measured for dense attention at 128 frames (% of bf16 peak): 4 waves x 3
 // workgroups x 3 stages 46.6; 12 x 1 x 3 (8 loading) 45.6; 8 x 1 x 5 43.2;
 // 6 x 2 x 3 38.8 (the register budget then allows only 2 waves per SIMD).
-template <int W, int G, int S, int D, int Q, bool P = false>
+template <int W, int G, int S, int D, int Q, int P = 1>
 struct TileCfg {
   static constexpr int waves = W;
   static constexpr int wg_per_cu = G;
   static constexpr int stages = S;
   static constexpr int dma_waves = D;
   static constexpr int halves = Q;  // 32-query halves per wave
-  static constexpr bool pairs = P;  // 4 stages refilled two at a time, one barrier per two tiles
+  static constexpr int group = P;   // > 1: 2P stages refilled P at a time, one barrier per P tiles
   static constexpr int threads = W * 64;
   static constexpr int block_m = W * 32 * Q;
   static constexpr int rows_per_wave = 64 / D;           // K rows and V^T rows per loading wave
   static constexpr int loads_per_tile = 2 * rows_per_wave / 8;  // 16-byte loads per lane
   static_assert(D <= W && 64 % D == 0 && rows_per_wave % 8 == 0, "load split");
   static_assert(S >= 2 && S <= 9, "ring");
-  static_assert(!P || S == 4, "pairs of tiles use a 4-stage ring");
+  static_assert(P == 1 || S == 2 * P, "groups of P tiles use a 2P-stage ring");
 };
 // GLOBAL: two 32-query halves per wave sharing every LDS operand read (64
 // queries a wave, 256 a workgroup, 2 workgroups = 2 waves per SIMD): measured
 // on a register/LDS-only probe of the tile arithmetic, 63% of the bf16 peak
 // against 51% for one half per wave at 3 waves per SIMD. FRAME/SUBSAMPLED keep
 // one half per wave (a frame's 1374 queries fill 128-query tiles better).
+// GLOBAL stages its tiles in groups of 2 (4 stages, a barrier per 2 tiles).
+// 8 waves x 512 queries x 1 workgroup per CU (groups of 2, 3 or 4 tiles) moves
+// half the bytes from L2 into LDS and runs at a 6-8% higher clock, but the two
+// waves of a SIMD then wait on each other at the barriers: no faster.
 template <int MODE>
 struct Cfg : TileCfg<4, 3, 3, 4, 1> {};
 template <>
-struct Cfg<0> : TileCfg<4, 2, 4, 4, 2, true> {};
+struct Cfg<0> : TileCfg<4, 2, 4, 4, 2, 2> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -412,12 +416,12 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
   // The whole key stream: clean(stage) for each tile of the main rounds (all
   // clean), rest(t, stage) for tile t of the others.
   //   ring:  kAhead tiles in flight; one wait and barrier per tile.
-  //   pairs: stages {0,1} and {2,3} alternate; at each barrier (every second
-  //          tile) the pair just freed is refilled with the tiles two ahead,
-  //          whose loads then have two tiles' time to land (as in a 3-stage
-  //          ring) -- half the barriers, for 4 stages of LDS.
+  //   groups of P tiles (P = C::group > 1): stages [0, P) and [P, 2P)
+  //          alternate; at each barrier (every P tiles) the group just freed
+  //          is refilled with the tiles P ahead, whose loads then have P
+  //          tiles' time to land -- a barrier per P tiles, for 2P stages.
   auto drive = [&](auto&& clean, auto&& rest) {
-    if constexpr (!C::pairs) {
+    if constexpr (C::group == 1) {
 #pragma unroll
       for (int j = 0; j < kAhead; ++j)
         if (j < n_tiles) issue_tile(tile_of(j), smem + j * kStageBytes);
@@ -430,29 +434,32 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
       }
       run_rest(rest);
     } else {
-      if (0 < n_tiles) issue_tile(tile_of(0), smem);
-      if (1 < n_tiles) issue_tile(tile_of(1), smem + kStageBytes);
-      // main rounds of 4 clean tiles; every tile issued ahead is clean too
-      const int n_main_p = max(0, n_clean - 2) / 4 * 4;
-      for (int j = 0; j < n_main_p; j += 4) {
+      constexpr int P = C::group;
+#pragma unroll
+      for (int i = 0; i < P; ++i)
+        if (i < n_tiles) issue_tile(tile_of(i), smem + i * kStageBytes);
+      // main rounds of 2P clean tiles; every tile issued ahead is clean too
+      const int n_main_g = max(0, n_clean - P) / (2 * P) * (2 * P);
+      for (int j = 0; j < n_main_g; j += 2 * P) {
         wait_and_meet<0>();
-        issue_tile(clean_tile(j + 2), smem + 2 * kStageBytes);
-        issue_tile(clean_tile(j + 3), smem + 3 * kStageBytes);
-        clean(smem);
-        clean(smem + kStageBytes);
+#pragma unroll
+        for (int i = 0; i < P; ++i) issue_tile(clean_tile(j + P + i), smem + (P + i) * kStageBytes);
+#pragma unroll
+        for (int i = 0; i < P; ++i) clean(smem + i * kStageBytes);
         wait_and_meet<0>();
-        issue_tile(clean_tile(j + 4), smem);
-        issue_tile(clean_tile(j + 5), smem + kStageBytes);
-        clean(smem + 2 * kStageBytes);
-        clean(smem + 3 * kStageBytes);
+#pragma unroll
+        for (int i = 0; i < P; ++i) issue_tile(clean_tile(j + 2 * P + i), smem + i * kStageBytes);
+#pragma unroll
+        for (int i = 0; i < P; ++i) clean(smem + (P + i) * kStageBytes);
       }
-      for (int j = n_main_p; j < n_tiles; j += 2) {
+      for (int j = n_main_g; j < n_tiles; j += P) {
         wait_and_meet<0>();
-        const int sj = j & 3;  // 0 or 2: the pair's first stage
-        if (j + 2 < n_tiles) issue_tile(tile_of(j + 2), smem + ((sj + 2) & 3) * kStageBytes);
-        if (j + 3 < n_tiles) issue_tile(tile_of(j + 3), smem + ((sj + 3) & 3) * kStageBytes);
-        rest(tile_of(j), smem + sj * kStageBytes);
-        if (j + 1 < n_tiles) rest(tile_of(j + 1), smem + (sj + 1) * kStageBytes);
+        const int sj = j % (2 * P);  // 0 or P: the group's first stage
+        const int so = P - sj;       // the other group's first stage
+        for (int i = 0; i < P; ++i)
+          if (j + P + i < n_tiles) issue_tile(tile_of(j + P + i), smem + (so + i) * kStageBytes);
+        for (int i = 0; i < P; ++i)
+          if (j + i < n_tiles) rest(tile_of(j + i), smem + (sj + i) * kStageBytes);
       }
     }
   };
