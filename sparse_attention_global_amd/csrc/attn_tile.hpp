@@ -389,6 +389,8 @@ struct FlashWaveState {
 // halves' independent chains (one half's probabilities while the other's
 // products run on the matrix core) give the scheduler work to overlap within
 // the wave. Per half the arithmetic is FlashWaveState's, in the same order.
+// The MFMAs go in a snake order (each shares its A or its B operand with the
+// one before: fewer operand bits toggle on a power-limited clock).
 struct FlashWaveState2 {
   FlashWaveState a, b;
 
@@ -412,14 +414,14 @@ struct FlashWaveState2 {
         for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = ld16(stage + off.k[ks] + kb * 32 * 128);
       sa[0] = mfma32(ka[0][0], qa[0], a.negm);
       sa[1] = mfma32(ka[1][0], qa[0], a.negm);
-      sb[0] = mfma32(ka[0][0], qb[0], a.negm);
       sb[1] = mfma32(ka[1][0], qb[0], a.negm);
+      sb[0] = mfma32(ka[0][0], qb[0], a.negm);
 #pragma unroll
       for (int ks = 1; ks < 4; ++ks) {
         sa[0] = mfma32(ka[0][ks], qa[ks], sa[0]);
         sa[1] = mfma32(ka[1][ks], qa[ks], sa[1]);
-        sb[0] = mfma32(ka[0][ks], qb[ks], sb[0]);
         sb[1] = mfma32(ka[1][ks], qb[ks], sb[1]);
+        sb[0] = mfma32(ka[0][ks], qb[ks], sb[0]);
       }
     }
     if constexpr (MASKED) {
@@ -451,12 +453,12 @@ struct FlashWaveState2 {
         b.l = sum_bf16x8(pb[mm], b.l);
       }
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          a.oacc[db] = mfma32(va[2 * db + mm], pa[mm], a.oacc[db]);
-          b.oacc[db] = mfma32(va[2 * db + mm], pb[mm], b.oacc[db]);
-        }
+      for (int mm = 0; mm < 2; ++mm) {
+        a.oacc[0] = mfma32(va[mm], pa[mm], a.oacc[0]);
+        b.oacc[0] = mfma32(va[mm], pb[mm], b.oacc[0]);
+        b.oacc[1] = mfma32(va[2 + mm], pb[mm], b.oacc[1]);
+        a.oacc[1] = mfma32(va[2 + mm], pa[mm], a.oacc[1]);
+      }
     }
   }
 };

@@ -603,7 +603,9 @@ static long long vt_ld_compact(const FlashLaunch& p) {
   return ((long long)p.g.n_frames * (p.mk + p.has_mean) + 63) / 64 * 64;
 }
 static int block_m(int mode) {
-  return mode == FLASH_GLOBAL ? Cfg<MODE_GLOBAL>::block_m : Cfg<MODE_FRAME>::block_m;
+  return mode == FLASH_GLOBAL ? Cfg<MODE_GLOBAL>::block_m
+         : mode == FLASH_FRAME ? Cfg<MODE_FRAME>::block_m
+                               : Cfg<MODE_SUBSAMPLED>::block_m;
 }
 static long long logical_workgroups(const FlashLaunch& p) {
   const int bm = block_m(p.mode);
