@@ -77,10 +77,16 @@ struct TileCfg {
 // 8 waves x 512 queries x 1 workgroup per CU (groups of 2, 3 or 4 tiles) moves
 // half the bytes from L2 into LDS and runs at a 6-8% higher clock, but the two
 // waves of a SIMD then wait on each other at the barriers: no faster.
-template <int MODE>
+// SUBSAMPLED runs a frame's queries in two launches (PART 0 and 1): the whole
+// 256-query tiles with two halves per wave, the rest of the frame (1374 = 5 x
+// 256 + 94) with one half per wave, so that no frame pays for a mostly empty
+// 256-query tile.
+template <int MODE, int PART = 0>
 struct Cfg : TileCfg<4, 3, 3, 4, 1> {};
 template <>
-struct Cfg<0> : TileCfg<4, 2, 4, 4, 2, 2> {};
+struct Cfg<0, 0> : TileCfg<4, 2, 4, 4, 2, 2> {};
+template <>
+struct Cfg<2, 0> : TileCfg<4, 2, 4, 4, 2, 2> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -121,6 +127,7 @@ struct FlashArgs {
   unsigned char* redo;  // [n_logical] 1: the workgroup's rows need the exact pass
   float scale_log2;  // log2(e) / sqrt(d)
   int n_qtiles;      // GLOBAL: tiles over T; else tiles per frame
+  int q_off, q_span; // FRAME/SUBSAMPLED: the query rows [q_off, q_off + q_span) of each frame
   int n_logical;     // logical workgroups
   int remap;         // 1: give each XCD a contiguous range of logical workgroups
 };
@@ -168,9 +175,9 @@ __device__ __forceinline__ void wait_and_meet() {
 // EXACT = false: the main pass against the logit bound; every workgroup records
 // in A.redo whether some row's probabilities underflowed. EXACT = true: only the
 // recorded workgroups run, redoing their rows with the exact online softmax.
-template <int MODE, bool EXACT>
+template <int MODE, bool EXACT, int PART>
 __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned char* smem) {
-  using C = Cfg<MODE>;
+  using C = Cfg<MODE, PART>;
   constexpr int kStages = C::stages;
   constexpr int kAhead = kStages - 1;  // tiles in flight ahead of the one consumed
   constexpr int kBlockM = C::block_m;
@@ -190,8 +197,8 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
     h = lid / per_head;
     const int rem = lid % per_head;
     f = rem / A.n_qtiles;
-    q0 = (long long)f * A.g.L + (long long)(rem % A.n_qtiles) * kBlockM;
-    q_end = min(q0 + kBlockM, (long long)(f + 1) * A.g.L);
+    q0 = (long long)f * A.g.L + A.q_off + (long long)(rem % A.n_qtiles) * kBlockM;
+    q_end = min(q0 + kBlockM, (long long)f * A.g.L + A.q_off + A.q_span);
   }
 
   // ---- key segments ----------------------------------------------------------
@@ -547,8 +554,8 @@ __device__ __forceinline__ void flash_tile(const FlashArgs& A, int lid, unsigned
 // FRAME/SUBSAMPLED mode). A persistent grid that keeps the resident
 // workgroups streaming the same keys in step was measured slower at every
 // size (1000 frames: 43.8-45.8% of the bf16 peak against 48-49%).
-template <int MODE, bool EXACT>
-__global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flash_bf16_kernel(
+template <int MODE, bool EXACT, int PART>
+__global__ __launch_bounds__((Cfg<MODE, PART>::threads), (Cfg<MODE, PART>::wg_per_cu)) void flash_bf16_kernel(
     FlashArgs A) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int lid = blockIdx.x;
@@ -556,7 +563,7 @@ __global__ __launch_bounds__(Cfg<MODE>::threads, Cfg<MODE>::wg_per_cu) void flas
     const int per = (A.n_logical + 7) >> 3;
     lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   }
-  flash_tile<MODE, EXACT>(A, lid, smem);
+  flash_tile<MODE, EXACT, PART>(A, lid, smem);
 }
 
 // Per (head, chunk) maximum of |k|^2 over the rows of K: a workgroup per
@@ -602,15 +609,42 @@ static long long vt_ld_compact(const FlashLaunch& p) {
   if (p.mode != FLASH_SUBSAMPLED) return 0;
   return ((long long)p.g.n_frames * (p.mk + p.has_mean) + 63) / 64 * 64;
 }
-static int block_m(int mode) {
-  return mode == FLASH_GLOBAL ? Cfg<MODE_GLOBAL>::block_m
-         : mode == FLASH_FRAME ? Cfg<MODE_FRAME>::block_m
-                               : Cfg<MODE_SUBSAMPLED>::block_m;
-}
-static long long logical_workgroups(const FlashLaunch& p) {
-  const int bm = block_m(p.mode);
-  if (p.mode == FLASH_GLOBAL) return (p.g.T + bm - 1) / bm * p.g.n_heads;
-  return (long long)((p.g.L + bm - 1) / bm) * p.g.n_frames * p.g.n_heads;
+// The launches of one call: the query rows [q_off, q_off + q_span) of every
+// frame (FRAME/SUBSAMPLED; GLOBAL: all of T) in tiles of block_m, with the
+// tile configuration `part` (Cfg<mode, part>).
+struct LaunchPart {
+  int part, block_m, q_off, q_span, n_qtiles;
+  long long n_logical;
+};
+static int launch_parts(const FlashLaunch& p, LaunchPart out[2]) {
+  if (p.mode == FLASH_GLOBAL) {
+    const int bm = Cfg<MODE_GLOBAL>::block_m;
+    const long long nq = (p.g.T + bm - 1) / bm;
+    out[0] = LaunchPart{0, bm, 0, 0, (int)min(nq, 0x7fffffffLL), nq * p.g.n_heads};
+    return 1;
+  }
+  const long long per_frame = (long long)p.g.n_frames * p.g.n_heads;
+  if (p.mode == FLASH_FRAME) {
+    const int bm = Cfg<MODE_FRAME>::block_m;
+    const int nq = (p.g.L + bm - 1) / bm;
+    out[0] = LaunchPart{0, bm, 0, p.g.L, nq, nq * per_frame};
+    return 1;
+  }
+  // SUBSAMPLED: whole two-half tiles, then the rest in one-half tiles when it
+  // fits one of them (else the two-half tiles cover the frame)
+  const int bm = Cfg<MODE_SUBSAMPLED, 0>::block_m, bt = Cfg<MODE_SUBSAMPLED, 1>::block_m;
+  const int rest = p.g.L % bm;
+  const int main_rows = (rest == 0 || rest > bt) ? p.g.L : p.g.L - rest;
+  int n = 0;
+  if (main_rows > 0) {
+    const int nq = (main_rows + bm - 1) / bm;
+    out[n++] = LaunchPart{0, bm, 0, main_rows, nq, nq * per_frame};
+  }
+  if (main_rows < p.g.L) {
+    const int nq = (p.g.L - main_rows + bt - 1) / bt;
+    out[n++] = LaunchPart{1, bt, main_rows, p.g.L - main_rows, nq, nq * per_frame};
+  }
+  return n;
 }
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -623,8 +657,26 @@ static size_t norm_bytes(const FlashLaunch& p) {
   return round256((size_t)p.g.n_heads * kNormChunks * sizeof(float));
 }
 
+// one redo flag byte per logical workgroup of each launch
+static size_t flag_bytes(const FlashLaunch& p) {
+  LaunchPart parts[2];
+  const int n = launch_parts(p, parts);
+  size_t b = 0;
+  for (int i = 0; i < n; ++i) b += round256((size_t)parts[i].n_logical);
+  return b;
+}
+
 size_t flash_bf16_workspace(const FlashLaunch& p) {
-  return vt_bytes(p) + norm_bytes(p) + round256((size_t)logical_workgroups(p));
+  return vt_bytes(p) + norm_bytes(p) + flag_bytes(p);
+}
+
+static bool parts_fit(const FlashLaunch& p) {
+  LaunchPart parts[2];
+  const int n = launch_parts(p, parts);
+  for (int i = 0; i < n; ++i)
+    if (parts[i].n_logical > 0x7ffffff0LL || (long long)parts[i].n_qtiles * parts[i].block_m > 0x7fffffffLL)
+      return false;
+  return true;
 }
 
 bool flash_bf16_fits(const FlashLaunch& p) {
@@ -632,8 +684,7 @@ bool flash_bf16_fits(const FlashLaunch& p) {
   const long long lim = 0x7fffffffLL;
   return (long long)kTileKeys * p.g.n_heads * kHeadDim * 2 <= lim &&
          (long long)kHeadDim * vt_ld_main(p) * 2 <= lim &&
-         (long long)kHeadDim * vt_ld_compact(p) * 2 <= lim &&
-         logical_workgroups(p) <= 0x7ffffff0LL;
+         (long long)kHeadDim * vt_ld_compact(p) * 2 <= lim && parts_fit(p);
 }
 
 hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream) {
@@ -654,14 +705,13 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   bf16* vt = reinterpret_cast<bf16*>(wsb);
   float* knorm2 = reinterpret_cast<float*>(wsb + vt_bytes(p));
-  A.redo = wsb + vt_bytes(p) + norm_bytes(p);
+  unsigned char* const redo = wsb + vt_bytes(p) + norm_bytes(p);
   A.vt = vt;
   A.vt_ld = vt_ld_main(p);
   hipError_t e;
   if (p.mode == FLASH_GLOBAL) {
     e = launch_vt_prepare(p.v, p.g.n_heads, p.n_keys, p.n_keys, A.vt_ld, A.vt_ld, vt, stream);
     if (e != hipSuccess) return e;
-    A.n_qtiles = (int)((p.g.T + block_m(p.mode) - 1) / block_m(p.mode));
     A.remap = 0;
   } else {
     A.vt_pitch = (p.g.L + 63) / 64 * 64;
@@ -677,7 +727,6 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
       if (e != hipSuccess) return e;
       A.cvt = cvt;
     }
-    A.n_qtiles = (p.g.L + block_m(p.mode) - 1) / block_m(p.mode);
     A.remap = 1;
   }
   // key-norm partials over every key the queries can meet (the compacted
@@ -689,26 +738,45 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
   if (e != hipSuccess) return e;
   A.knorm2 = knorm2;
   A.bound_extra = (p.mode == FLASH_SUBSAMPLED && p.has_mean) ? p.mean_bias2 : 0.f;
-  A.n_logical = (int)logical_workgroups(p);
-  const int grid = A.remap ? ((A.n_logical + 7) / 8) * 8 : A.n_logical;
-  // the main pass, then the exact pass over the workgroups it flagged
-  auto launch = [&](auto kernel, auto cfg) {
-    using C = decltype(cfg);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::threads), C::stages * kStageBytes, stream, A);
-  };
-  switch (p.mode) {
-    case FLASH_GLOBAL:
-      launch(flash_bf16_kernel<MODE_GLOBAL, false>, Cfg<MODE_GLOBAL>{});
-      launch(flash_bf16_kernel<MODE_GLOBAL, true>, Cfg<MODE_GLOBAL>{});
-      break;
-    case FLASH_FRAME:
-      launch(flash_bf16_kernel<MODE_FRAME, false>, Cfg<MODE_FRAME>{});
-      launch(flash_bf16_kernel<MODE_FRAME, true>, Cfg<MODE_FRAME>{});
-      break;
-    default:
-      launch(flash_bf16_kernel<MODE_SUBSAMPLED, false>, Cfg<MODE_SUBSAMPLED>{});
-      launch(flash_bf16_kernel<MODE_SUBSAMPLED, true>, Cfg<MODE_SUBSAMPLED>{});
-      break;
+  // per launch part: the main pass, then the exact pass over the workgroups
+  // it flagged (each part with its own redo flags)
+  LaunchPart parts[2];
+  const int n_parts = launch_parts(p, parts);
+  size_t flag_off = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    const LaunchPart& lp = parts[i];
+    A.n_qtiles = lp.n_qtiles;
+    A.q_off = lp.q_off;
+    A.q_span = lp.q_span;
+    A.n_logical = (int)lp.n_logical;
+    A.redo = redo + flag_off;
+    flag_off += round256((size_t)lp.n_logical);
+    const int grid = A.remap ? ((A.n_logical + 7) / 8) * 8 : A.n_logical;
+    auto launch = [&](auto kernel, auto cfg) {
+      using C = decltype(cfg);
+      hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::threads), C::stages * kStageBytes, stream, A);
+    };
+    switch (p.mode) {
+      case FLASH_GLOBAL:
+        launch(flash_bf16_kernel<MODE_GLOBAL, false, 0>, Cfg<MODE_GLOBAL>{});
+        launch(flash_bf16_kernel<MODE_GLOBAL, true, 0>, Cfg<MODE_GLOBAL>{});
+        break;
+      case FLASH_FRAME:
+        launch(flash_bf16_kernel<MODE_FRAME, false, 0>, Cfg<MODE_FRAME>{});
+        launch(flash_bf16_kernel<MODE_FRAME, true, 0>, Cfg<MODE_FRAME>{});
+        break;
+      default:
+        if (lp.part == 0) {
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, false, 0>, Cfg<MODE_SUBSAMPLED, 0>{});
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, true, 0>, Cfg<MODE_SUBSAMPLED, 0>{});
+        } else {
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, false, 1>, Cfg<MODE_SUBSAMPLED, 1>{});
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, true, 1>, Cfg<MODE_SUBSAMPLED, 1>{});
+        }
+        break;
+    }
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) return le;
   }
   return hipGetLastError();
 }

@@ -170,10 +170,13 @@ def test_workspace_sizes():
     assert _ws(g, 2, 0, 1) == (OK, 16 * 64 * 1408 * 256 * 2 + norms + frame_flags)
     assert _ws(g, 2, 5, 1)[0] == INVALID
     # subsampled: per frame 5 specials + 100 kept + 1 mean = 106 rows of K and V,
-    # then the frame-padded V^T and the V^T of the 27,136 compacted rows
+    # then the frame-padded V^T and the V^T of the 27,136 compacted rows; a
+    # frame's queries run as 5 workgroups of 256 and one of 128 (94 rows), each
+    # launch with its own redo flags
     half = r256(256 * 106 * 16 * 64 * 2)
+    sub_flags = r256(5 * 256 * 16) + r256(1 * 256 * 16)
     flash = r256(16 * 64 * 1408 * 256 * 2 + 16 * 64 * ((256 * 106 + 63) // 64 * 64) * 2 + norms
-                 + frame_flags)
+                 + sub_flags)
     assert _ws(g, 1, 4, 4) == (OK, 2 * half + flash)
     assert sga.compact_rows(g, 4, 4) == (105, 1)
     # fp32 keeps only the compacted set, dense needs nothing
