@@ -58,6 +58,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--variant-steps", type=int, default=1,
                     help="timed passes of each GSA variant after one untimed pass (0 skips them)")
+    ap.add_argument("--cpu-report", default="",
+                    help="only run the CPU-baseline leg over every configuration (the fp64 "
+                         "oracle on this host: the whole layer at 4 and 32 frames, 4096 seeded "
+                         "rows at 128, 256 and 1000 frames) and write its JSON to this path")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times) "
                          "so hardware byte counters can be scaled against known traffic")
@@ -79,6 +83,9 @@ def main():
     args = parse()
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.cpu_report:
+        cpu_report(args.cpu_report, args.seed)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the sharded multi-GPU "
@@ -513,6 +520,75 @@ def cpu_baseline(q, k, v, w, b, geom, wl, rows_per_form, seed, layers):
                      f"subsampled incl. its whole compaction), fp64 NumPy oracle, {workers} threads; "
                      f"{total_s:.1f} s")
     return out
+
+
+def cpu_report(path, seed):
+    """The CPU-baseline leg over every configuration: the fp64 oracle, as it
+    stands, timed on this host's cores (no GPU is used). The whole layer where
+    it is affordable (4 frames, fp32; 32 frames), else 4096 seeded query rows
+    (all heads) with the full layer extrapolated from the measured rate."""
+    import contextlib
+    import io
+    import numpy as np
+    import oracle
+    from synth import WORKLOADS, make_gate, make_qkv, sample_rows
+
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        host_cores = os.cpu_count() or 1
+    workers = max(1, min(16, host_cores))
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        np.show_config()
+    plan = [("tiny", ("dense", "frame", "gsa", "subsampled"), None),
+            ("dense32", ("dense", "frame"), None),
+            ("gsa128", ("dense", "gsa"), 4096),
+            ("sga256", ("dense", "frame", "subsampled"), 4096),
+            ("scene1000", ("dense", "frame", "gsa", "subsampled"), 4096)]
+    out = {"kind": "oracle", "host_cores": host_cores, "oracle_threads": workers,
+           "numpy": np.__version__, "numpy_config": buf.getvalue(), "configs": {}}
+    for name, forms, n_rows in plan:
+        wl = WORKLOADS[name]
+        g = wl.geom
+        q, k, v = make_qkv(g, seed=seed, device="cpu", distribution=wl.distribution)
+        w, b = make_gate(g.n_heads, g.head_dim, seed=seed, device="cpu")
+        qh, kh, vh = (x.float().numpy() for x in (q, k, v))
+        wh, bh = w.numpy(), b.numpy()
+        del q, k, v
+        T = g.n_tokens
+        rows = None if n_rows is None else sample_rows(T, n_rows, seed=seed + 7).numpy()
+        sh, sw = wl.stride
+        calls = {
+            "dense": lambda r: oracle.dense_attention(qh, kh, vh, rows=r, workers=workers),
+            "frame": lambda r: oracle.frame_attention(qh, kh, vh, g, rows=r),
+            "gsa": lambda r: oracle.gsa_layer(qh, kh, vh, g, wh, bh, wl.top_k, rows=r, workers=workers),
+            "subsampled": lambda r: oracle.subsampled_attention(qh, kh, vh, g, sh, sw, rows=r,
+                                                                workers=workers),
+        }
+        res = {"frames": g.n_frames, "tokens": T, "heads": g.n_heads, "dtype": g.dtype,
+               "rows": T if rows is None else len(rows)}
+        all_rows = np.arange(T) if rows is None else rows
+        for form in forms:
+            # in parts of about 1024 rows, each reported (the GSA layer pools the
+            # whole batch on every call, so it runs in one part)
+            parts = [all_rows] if form == "gsa" else np.array_split(all_rows, max(1, len(all_rows) // 1024))
+            dt = 0.0
+            for part in parts:
+                t0 = time.perf_counter()
+                calls[form](None if (rows is None and len(parts) == 1) else part)
+                dt += time.perf_counter() - t0
+                print(f"[cpu-report] {name} {form}: part of {len(part)} rows done", file=sys.stderr,
+                      flush=True)
+            n = T if rows is None else len(rows)
+            res[form] = {"seconds": dt, "rows_per_s": n / dt,
+                         "full_layer_s": dt if rows is None else T * dt / n,
+                         "full_layer": "measured" if rows is None else "extrapolated"}
+            print(f"[cpu-report] {name} {form}: {n} rows in {dt:.1f} s", file=sys.stderr, flush=True)
+        out["configs"][name] = res
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps({k: v for k, v in out.items() if k != "numpy_config"}), flush=True)
 
 
 def small_config_speedups(sga, torch, make_qkv, make_gate, seed, dev):
