@@ -536,6 +536,29 @@ def test_subsampled_token_diagonal(geom, stride):
         assert_close(host(o), oracle.dense_attention(qh, kh, vh), geom.dtype, "token diagonal stride 1")
 
 
+@pytest.mark.parametrize("geom", [
+    pytest.param(Geometry(2, 0, 16, 16, 2, 64, "bf16"), id="L256-whole-tiles"),
+    pytest.param(Geometry(2, 4, 16, 18, 2, 64, "bf16"), id="L292-split"),
+    pytest.param(Geometry(2, 0, 20, 20, 2, 64, "bf16"), id="L400-partial-256-tile"),
+    pytest.param(Geometry(3, 0, 8, 16, 2, 64, "bf16"), id="L128-rest-only"),
+])
+def test_subsampled_query_tiling(geom):
+    """The subsampled form runs a frame's whole 256-query tiles and the rest
+    (at most 128 rows) in two launches, or one launch when the rest is empty,
+    longer than 128 rows or the whole frame: every row of each case, modes 0
+    and 2, against the oracle."""
+    _announce(f"subsampled query tiling {geom}")
+    q, k, v = make_qkv(geom, seed=73, device=DEV, distribution="scene")
+    o0 = sga.subsampled_global_attn(q, k, v, geom, 2, 2, mode=0, mean_log_count=True)
+    o2 = sga.subsampled_global_attn(q, k, v, geom, 2, 2, mode=2)
+    _sync()
+    qh, kh, vh = host(q), host(k), host(v)
+    assert_close(host(o0), oracle.subsampled_attention(qh, kh, vh, geom, 2, 2, mean_log_count=True),
+                 "bf16", "subsampled tiling mode 0")
+    assert_close(host(o2), oracle.subsampled_attention(qh, kh, vh, geom, 2, 2, mode=2), "bf16",
+                 "subsampled tiling mode 2")
+
+
 @pytest.mark.parametrize("geom,top_k", [
     pytest.param(Geometry(3, 5, 13, 11, 2, 64, "bf16"), 5, id="ragged-bf16"),
     pytest.param(Geometry(2, 2, 9, 9, 3, 64, "f32"), 3, id="ragged-f32"),
