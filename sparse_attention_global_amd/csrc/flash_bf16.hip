@@ -8,10 +8,13 @@
 //   SUBSAMPLED  AVGGT subsampled attention: the own frame whole, then the
 //               compacted set of all frames with the own frame's rows masked.
 //
-// Work split: a workgroup of 4 waves owns 128 consecutive query rows of one
-// head (never straddling a frame in FRAME/SUBSAMPLED mode); each wave owns 32.
-// The per-tile math (attn_tile.hpp) keeps every per-query quantity inside the
-// lane that owns the query.
+// Work split: a workgroup of 4 waves owns consecutive query rows of one head
+// (never straddling a frame in FRAME/SUBSAMPLED mode): 256 in GLOBAL mode and
+// for a frame's whole 256-row tiles in SUBSAMPLED mode (each wave 64, as two
+// 32-query halves sharing every K/V^T operand read), 128 in FRAME mode and for
+// the rest of a SUBSAMPLED frame (each wave 32). The per-tile math
+// (attn_tile.hpp) keeps every per-query quantity inside the lane that owns the
+// query.
 //
 // Softmax: the scale log2(e)/sqrt(d) is folded into Q (rounded once to bf16),
 // and every query starts its accumulator at minus an upper bound of its logits,
@@ -25,7 +28,8 @@
 // Data movement: keys stream in tiles of 64 through a ring of LDS stages.
 // Every K row and every V^T row of a tile moves from HBM/L2 straight into LDS
 // with 16-byte direct buffer loads (buffer_load_dwordx4 ... lds) issued two
-// tiles ahead -- no registers, no VALU address work per tile, no LDS write
+// tiles ahead (in the two-half configuration two tiles at a time, one barrier
+// per two tiles) -- no registers, no VALU address work per tile, no LDS write
 // instructions. The swizzled LDS layouts are produced by choosing which
 // 16-byte chunk each lane fetches. V^T comes from a staging pass (vt_prepare)
 // that already holds V transposed in the MFMA operand's key order. A tile is
@@ -96,7 +100,8 @@ constexpr float kBoundMargin = 1.0078125f;  // 1 + 2^-7
 // A row whose probabilities against the bound sum below this is redone exactly:
 // every key then within 2^-25 of the row's total weight is a normal float.
 constexpr float kLooseBoundSum = 8.271806125530277e-25f;  // 2^-80
-// Occupancy: 3 workgroups (12 waves) per CU with a 3-stage LDS ring (144 KiB).
+// Occupancy of the one-half configuration (FRAME, the rest of a SUBSAMPLED
+// frame): 3 workgroups (12 waves) per CU with a 3-stage LDS ring (144 KiB).
 // Measured on MI355X at 128 frames (dense attention, % of bf16 peak): 3 stages
 // and 3 workgroups 44-46%; 2 / 3 43%; 2 / 4, where the 128-VGPR budget makes the
 // compiler spill inside the tile loop, 37%. A ping-pong schedule of two
