@@ -1750,7 +1750,10 @@ hipError_t launch_gsa_topk(const Geom& g, const float* q_blk, const float* k_cmp
                          stream, g, q_blk, planes, n_total, n_cand, first, top_k, n_rowtiles, idx, score, fl);
     }
     if (hipError_t e = hipGetLastError()) return e;
+    // (no split capacity -- the allocation-free entry point on its largest
+    // problems -- leaves nothing to merge)
     const long long mwaves = (long long)g.n_heads * lay.cap;
+    if (mwaves == 0) return hipSuccess;
     hipLaunchKernelGGL(gsa_topk_seg_merge_kernel, dim3((unsigned)((mwaves + 3) / 4)), dim3(256), 0, stream, g,
                        top_k, lay.cap, fail_rows, fail_count, fl.seg_val, fl.seg_idx, idx, score);
     return hipGetLastError();

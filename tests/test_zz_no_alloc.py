@@ -49,6 +49,21 @@ def test_noalloc_matches_workspace_entry(top_k):
         del q32, k32
 
 
+def test_noalloc_no_split_capacity():
+    """At 209 frames and 16 heads the selection scratch leaves the fallback no
+    split capacity (the next 128 listed rows would not fit): every block that
+    misses the certificate streams all keys in one workgroup, and the result
+    still equals the workspace entry point's (split fallback, merged)."""
+    geom = Geometry(209, 5, 37, 37, 16, 64, "bf16")
+    print(f"[case] noalloc, no split capacity: {geom}", flush=True)
+    q32, k32 = _inputs(geom, seed=61)
+    want_i, want_s = sga.gsa_select_topk(q32, k32, geom, 16, want_score=True)
+    got_i, got_s = sga.gsa_select_topk_noalloc(q32, k32, geom, 16, want_score=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got_i, want_i)
+    assert torch.equal(got_s, want_s)
+
+
 def test_noalloc_all_ties_fallback():
     """Every block misses the certificate (all pooled keys equal), so the exact
     fallback runs with the capacity the scratch leaves it; ties go to the
