@@ -593,8 +593,8 @@ def cpu_report(path, seed):
 
 def small_config_speedups(sga, torch, make_qkv, make_gate, seed, dev):
     """The GSA form at 128 frames and the subsampled form at 256 frames against
-    dense attention at the same size (one untimed call each, then the median of
-    three timed ones)."""
+    dense attention at the same size, and every form at 4 frames (fp32) and 32
+    frames (one untimed call each, then the median of three timed ones)."""
     from synth import WORKLOADS
 
     def timed(fn):
@@ -631,6 +631,28 @@ def small_config_speedups(sga, torch, make_qkv, make_gate, seed, dev):
               f"{t_x:.1f} ms ({t_d / t_x:.1f}x)", file=sys.stderr, flush=True)
         del q, k, v
         torch.cuda.empty_cache()
+    # the two configurations parity runs on whole: 4 frames in fp32 (one head,
+    # every form) and 32 frames in bf16 (dense and frame attention)
+    for name in ("tiny", "dense32"):
+        wl = WORKLOADS[name]
+        g = wl.geom
+        q, k, v = make_qkv(g, seed=seed, device=dev, distribution=wl.distribution)
+        sh, sw = wl.stride
+        forms = {"dense": lambda: sga.dense_global_attn(q, k, v, g),
+                 "frame": lambda: sga.dense_global_attn(q, k, v, g, frame_local=True)}
+        if name == "tiny":
+            w, b = make_gate(g.n_heads, g.head_dim, seed=seed, device=dev)
+            forms["gsa"] = lambda: sga.gsa_layer(q, k, v, w, b, g, wl.top_k)
+            forms["subsampled"] = lambda: sga.subsampled_global_attn(q, k, v, g, sh, sw)
+        T = g.n_tokens
+        res = {"frames": g.n_frames, "heads": g.n_heads, "dtype": g.dtype}
+        for form, fn in forms.items():
+            t = timed(fn)
+            res[form] = {"ms": t, "tokens_per_s": T / t * 1e3}
+        out[name] = res
+        print(f"[bench] {name}: " + ", ".join(f"{f} {res[f]['ms']:.3f} ms" for f in forms),
+              file=sys.stderr, flush=True)
+        del q, k, v
     return out
 
 

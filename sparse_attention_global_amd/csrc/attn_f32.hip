@@ -1,7 +1,10 @@
 // fp32 attention of the forms the bf16 flash kernel serves (dense/compressed,
-// frame, AVGGT subsampled), for fp32 layers: one thread per (query, head),
-// exact online softmax (expf), every product and sum in fp32. The key set and
-// its order follow the same definitions as the bf16 kernel.
+// frame, AVGGT subsampled), for fp32 layers: a workgroup of kSplit waves per
+// 64 queries and one head; lane l of every wave owns query l, and wave w visits
+// the w-th of every kSplit consecutive keys of the query's key set with an
+// exact online softmax (expf, every product and sum in fp32). The waves' partial
+// results (running maximum, sum and unnormalised output) then merge through
+// LDS. The key set follows the same definitions as the bf16 kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,18 +29,25 @@ struct F32Args {
   int s_h, s_w;
 };
 
-__global__ __launch_bounds__(64) void flash_f32_kernel(F32Args A) {
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int kSplit = 8;  // waves per workgroup, each visiting every kSplit-th key
+
+__global__ __launch_bounds__(64 * kSplit) void flash_f32_kernel(F32Args A) {
+  __shared__ float part[kSplit][kHeadDim + 2][64];  // per wave: acc[d], m, l of each lane's query
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long t = (long long)blockIdx.x * 64 + lane;
   const int h = blockIdx.y;
-  if (t >= A.g.T) return;
+  const bool valid = t < A.g.T;
   const long long rs = (long long)A.g.n_heads * kHeadDim;
   const long long hoff = (long long)h * kHeadDim;
-  const int f = (int)(t / A.g.L);
+  const long long tq = valid ? t : 0;
+  const int f = (int)(tq / A.g.L);
   float qv[kHeadDim], acc[kHeadDim];
-  const float* qp = A.q + t * rs + hoff;
+  const float* qp = A.q + tq * rs + hoff;
   for (int e = 0; e < kHeadDim; ++e) { qv[e] = qp[e] * 0.125f; acc[e] = 0.f; }
   float m = -INFINITY, l = 0.f;
+  unsigned int seq = 0;  // position of the next key in the query's key set
   auto visit = [&](const float* kp, const float* vp, float bias) {
+    if ((seq++ % kSplit) != (unsigned int)wave) return;
     float s = bias;
     for (int e = 0; e < kHeadDim; ++e) s = fmaf(qv[e], kp[e], s);
     const float m_new = fmaxf(m, s);
@@ -66,15 +76,34 @@ __global__ __launch_bounds__(64) void flash_f32_kernel(F32Args A) {
           visit(A.ck + r * rs + hoff, A.cv + r * rs + hoff, A.mean_bias);
         }
       if (diag) {  // the query's own key when its patch was dropped
-        const int p = (int)(t - f0) - A.g.n_special;
+        const int p = (int)(tq - f0) - A.g.n_special;
         if (p >= 0 && ((p / A.g.grid_w) % A.s_h != 0 || (p % A.g.grid_w) % A.s_w != 0))
-          visit(A.k + t * rs + hoff, A.v + t * rs + hoff, 0.f);
+          visit(A.k + tq * rs + hoff, A.v + tq * rs + hoff, 0.f);
       }
     }
   }
+  // merge the waves' partial results: M = max m_w, L = sum l_w e^(m_w - M),
+  // O = sum acc_w e^(m_w - M) / L (a wave that met no key has m_w = -inf, l_w = 0)
+  for (int e = 0; e < kHeadDim; ++e) part[wave][e][lane] = acc[e];
+  part[wave][kHeadDim][lane] = m;
+  part[wave][kHeadDim + 1][lane] = l;
+  __syncthreads();
+  if (wave != 0 || !valid) return;
+  float mm = -INFINITY;
+  for (int w = 0; w < kSplit; ++w) mm = fmaxf(mm, part[w][kHeadDim][lane]);
+  float sc[kSplit], ll = 0.f;
+  for (int w = 0; w < kSplit; ++w) {
+    const float mw = part[w][kHeadDim][lane];
+    sc[w] = mw == -INFINITY ? 0.f : expf(mw - mm);
+    ll = fmaf(part[w][kHeadDim + 1][lane], sc[w], ll);
+  }
   float* op = A.o + t * rs + hoff;
-  for (int e = 0; e < kHeadDim; ++e) op[e] = acc[e] / l;
-  if (A.lse) A.lse[t * A.g.n_heads + h] = m + logf(l);
+  for (int e = 0; e < kHeadDim; ++e) {
+    float o = 0.f;
+    for (int w = 0; w < kSplit; ++w) o = fmaf(part[w][e][lane], sc[w], o);
+    op[e] = o / ll;
+  }
+  if (A.lse) A.lse[t * A.g.n_heads + h] = mm + logf(ll);
 }
 
 }  // namespace
@@ -98,7 +127,7 @@ hipError_t launch_flash_f32(const FlashLaunch& p, hipStream_t stream) {
   A.s_h = p.s_h > 0 ? p.s_h : 1;
   A.s_w = p.s_w > 0 ? p.s_w : 1;
   dim3 grid((unsigned)((p.g.T + 63) / 64), (unsigned)p.g.n_heads);
-  hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(64), 0, stream, A);
+  hipLaunchKernelGGL(flash_f32_kernel, grid, dim3(64 * kSplit), 0, stream, A);
   return hipGetLastError();
 }
 
