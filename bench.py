@@ -546,7 +546,8 @@ def cpu_report(path, seed):
             ("gsa128", ("dense", "gsa"), 4096),
             ("sga256", ("dense", "frame", "subsampled"), 4096),
             ("scene1000", ("dense", "frame", "gsa", "subsampled"), 4096)]
-    out = {"kind": "oracle", "host_cores": host_cores, "oracle_threads": workers,
+    out = {"command": f"python bench.py --cpu-report {path}", "kind": "oracle", "host_cores": host_cores,
+           "oracle_threads": workers,
            "numpy": np.__version__, "numpy_config": buf.getvalue(), "configs": {}}
     for name, forms, n_rows in plan:
         wl = WORKLOADS[name]
