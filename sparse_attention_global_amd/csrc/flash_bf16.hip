@@ -91,6 +91,10 @@ template <>
 struct Cfg<0, 0> : TileCfg<4, 2, 4, 4, 2, 2> {};
 template <>
 struct Cfg<2, 0> : TileCfg<4, 2, 4, 4, 2, 2> {};
+// the rest of a SUBSAMPLED frame when it fits 96 rows: 3 waves (2 of them
+// loading the tiles), 3 workgroups per CU
+template <>
+struct Cfg<2, 2> : TileCfg<3, 3, 3, 2, 1> {};
 constexpr int kStageBytes = kTileKBytes + kTileVBytes;
 // Key-norm partial maxima per head (the logit bound's max|k|).
 constexpr int kNormChunks = 256;
@@ -635,9 +639,10 @@ static int launch_parts(const FlashLaunch& p, LaunchPart out[2]) {
     out[0] = LaunchPart{0, bm, 0, p.g.L, nq, nq * per_frame};
     return 1;
   }
-  // SUBSAMPLED: whole two-half tiles, then the rest in one-half tiles when it
-  // fits one of them (else the two-half tiles cover the frame)
-  const int bm = Cfg<MODE_SUBSAMPLED, 0>::block_m, bt = Cfg<MODE_SUBSAMPLED, 1>::block_m;
+  // SUBSAMPLED: whole two-half tiles, then the rest in one one-half tile of 96
+  // or 128 rows when it fits one (else the two-half tiles cover the frame)
+  const int bm = Cfg<MODE_SUBSAMPLED, 0>::block_m, bt = Cfg<MODE_SUBSAMPLED, 1>::block_m,
+            bs = Cfg<MODE_SUBSAMPLED, 2>::block_m;
   const int rest = p.g.L % bm;
   const int main_rows = (rest == 0 || rest > bt) ? p.g.L : p.g.L - rest;
   int n = 0;
@@ -646,8 +651,9 @@ static int launch_parts(const FlashLaunch& p, LaunchPart out[2]) {
     out[n++] = LaunchPart{0, bm, 0, main_rows, nq, nq * per_frame};
   }
   if (main_rows < p.g.L) {
-    const int nq = (p.g.L - main_rows + bt - 1) / bt;
-    out[n++] = LaunchPart{1, bt, main_rows, p.g.L - main_rows, nq, nq * per_frame};
+    const int r = p.g.L - main_rows;  // 1 .. bt rows: one tile
+    const int part = r <= bs ? 2 : 1;
+    out[n++] = LaunchPart{part, part == 2 ? bs : bt, main_rows, r, 1, per_frame};
   }
   return n;
 }
@@ -774,9 +780,12 @@ hipError_t launch_flash_bf16(const FlashLaunch& p, void* ws, hipStream_t stream)
         if (lp.part == 0) {
           launch(flash_bf16_kernel<MODE_SUBSAMPLED, false, 0>, Cfg<MODE_SUBSAMPLED, 0>{});
           launch(flash_bf16_kernel<MODE_SUBSAMPLED, true, 0>, Cfg<MODE_SUBSAMPLED, 0>{});
-        } else {
+        } else if (lp.part == 1) {
           launch(flash_bf16_kernel<MODE_SUBSAMPLED, false, 1>, Cfg<MODE_SUBSAMPLED, 1>{});
           launch(flash_bf16_kernel<MODE_SUBSAMPLED, true, 1>, Cfg<MODE_SUBSAMPLED, 1>{});
+        } else {
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, false, 2>, Cfg<MODE_SUBSAMPLED, 2>{});
+          launch(flash_bf16_kernel<MODE_SUBSAMPLED, true, 2>, Cfg<MODE_SUBSAMPLED, 2>{});
         }
         break;
     }

@@ -538,15 +538,16 @@ def test_subsampled_token_diagonal(geom, stride):
 
 @pytest.mark.parametrize("geom", [
     pytest.param(Geometry(2, 0, 16, 16, 2, 64, "bf16"), id="L256-whole-tiles"),
-    pytest.param(Geometry(2, 4, 16, 18, 2, 64, "bf16"), id="L292-split"),
+    pytest.param(Geometry(2, 4, 16, 18, 2, 64, "bf16"), id="L292-split-96"),
+    pytest.param(Geometry(2, 4, 16, 22, 2, 64, "bf16"), id="L356-split-128"),
     pytest.param(Geometry(2, 0, 20, 20, 2, 64, "bf16"), id="L400-partial-256-tile"),
     pytest.param(Geometry(3, 0, 8, 16, 2, 64, "bf16"), id="L128-rest-only"),
 ])
 def test_subsampled_query_tiling(geom):
     """The subsampled form runs a frame's whole 256-query tiles and the rest
-    (at most 128 rows) in two launches, or one launch when the rest is empty,
-    longer than 128 rows or the whole frame: every row of each case, modes 0
-    and 2, against the oracle."""
+    (one tile of 96 or 128 rows) in two launches, or one launch when the rest
+    is empty, longer than 128 rows or the whole frame: every row of each case,
+    modes 0 and 2, against the oracle."""
     _announce(f"subsampled query tiling {geom}")
     q, k, v = make_qkv(geom, seed=73, device=DEV, distribution="scene")
     o0 = sga.subsampled_global_attn(q, k, v, geom, 2, 2, mode=0, mean_log_count=True)
